@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the fp9 routed-expert MoE layer on one MI355X.
+
+Workload: one DeepSeek-V3-shaped MoE layer (hidden 7168, intermediate 2048,
+256 routed experts + 1 shared, top-8) with fp9 expert weights resident in HBM,
+decode batch 1 (and 2, reported alongside).  A step is one full layer call
+(gate/up + SwiGLU + down + combine) on a fresh seeded routing draw, so each
+step streams the selected experts from HBM rather than from cache.
+
+Prints one JSON line.  `value` is layer tokens/s at bsz 1 with inputs already
+in HBM.  The roofline object is for the dominant kernel (gate/up: two thirds
+of the bytes), timed with HIP events on the stream it runs on.  The CPU
+baseline is the float64 oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+H, I, E, K = 7168, 2048, 256, 8
+SEED, WORKLOAD = 0, 3
+METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=4,
+                   help="tokens (bsz 1 steps) the oracle times for the CPU baseline")
+    p.add_argument("--bsz2", type=int, default=1, help="also time bsz 2 (0 to skip)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def time_layer(torch, dm, layer, T, steps, warmup, draws):
+    """Times `steps` layer calls (after `warmup`) with events around both launches."""
+    from bit_moe_expert_fp9_amd import synth
+    n = steps + warmup
+    xs, ids, ws_, uniq = [], [], [], []
+    for s in range(n):
+        d = s % draws
+        x = synth.activations(SEED, WORKLOAD, 0, 10_000 + d, T, H)
+        i, w = synth.routing(SEED, WORKLOAD, 0, 10_000 + d, T, E, K)
+        xs.append(x)
+        ids.append(i)
+        ws_.append(w)
+        uniq.append(len(np.unique(i)))
+    X = torch.from_numpy(np.stack(xs)).cuda()
+    IDS = torch.from_numpy(np.stack(ids)).cuda()
+    W = torch.from_numpy(np.stack(ws_)).cuda()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T)
+    stream = torch.cuda.current_stream()
+
+    for s in range(warmup):
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        s = warmup + k
+        ev[2 * k].record(stream)
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+        ev[2 * k + 1].record(stream)
+        dm.moe_down(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+    ev[2 * steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev[0].elapsed_time(ev[2 * steps])
+    t_gu = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)])
+    t_dn = np.array([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(steps)])
+    u = np.array(uniq[warmup:], dtype=np.float64)
+    eb = layer.expert_bytes()
+    bytes_gu = (u + 1) * (2 * eb / 3) + T * H * 4
+    bytes_dn = (u + 1) * (eb / 3) + T * H * 4
+    return {
+        "T": T,
+        "total_ms": total_ms,
+        "wall_s": wall,
+        "ms_per_step": total_ms / steps,
+        "tokens_per_s": T * steps / (total_ms / 1e3),
+        "gate_up_us": float(t_gu.mean() * 1e3),
+        "down_us": float(t_dn.mean() * 1e3),
+        "bytes_gate_up": float(bytes_gu.mean()),
+        "bytes_down": float(bytes_dn.mean()),
+        "bytes_step": float((bytes_gu + bytes_dn).mean()),
+        "mean_experts": float((u + 1).mean()),
+        "p10_us": float(np.percentile(t_gu + t_dn, 10) * 1e3),
+        "p50_us": float(np.percentile(t_gu + t_dn, 50) * 1e3),
+        "p90_us": float(np.percentile(t_gu + t_dn, 90) * 1e3),
+    }
+
+
+def cpu_baseline(n_tokens):
+    """The float64 oracle on `n_tokens` bsz-1 steps of the same layer (1 thread)."""
+    import oracle
+    from bit_moe_expert_fp9_amd import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import OracleExperts
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ox = OracleExperts(SEED, WORKLOAD, 0, H, I)
+    draws = [(synth.activations(SEED, WORKLOAD, 0, 20_000 + s, 1, H),
+              *synth.routing(SEED, WORKLOAD, 0, 20_000 + s, 1, E, K)) for s in range(n_tokens)]
+    need = set([E])
+    for _, ids, _ in draws:
+        need.update(int(i) for i in ids.ravel())
+    log("cpu baseline: quantizing %d experts for the oracle (untimed)" % len(need))
+    ox.prefetch(sorted(need))
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        for x, ids, w in draws:
+            oracle.moe_layer(ox, x, ids, w, E)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d bsz-1 steps of the same 256+1-expert layer (fp9 decode + "
+                      "float64 SwiGLU experts, %.1f s), numpy with 1 BLAS thread" % (n_tokens, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_moe_expert_fp9_amd as dm
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dm.lib()  # raises if the library is not built
+
+    log("building layer: %d routed + 1 shared experts, fp9, %.2f GB" %
+        (E, (E + 1) * 3 * H * I * 9 / 8 / 1e9))
+    t0 = time.time()
+    layer = dm.Layer(H, I, E, K).fill_synthetic(SEED, WORKLOAD, 0)
+    log("layer ready in %.1f s" % (time.time() - t0))
+
+    draws = 512
+    r1 = time_layer(torch, dm, layer, 1, args.steps, args.warmup, draws)
+    log("bsz1:", json.dumps(r1))
+    r2 = None
+    if args.bsz2:
+        r2 = time_layer(torch, dm, layer, 2, args.steps, args.warmup, draws)
+        log("bsz2:", json.dumps(r2))
+
+    gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
+    gu_gbps = r1["bytes_gate_up"] / (r1["gate_up_us"] * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": r1["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r1["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "fp9 routed MoE layer, bsz 1 (7168/2048, 256 routed + 1 shared, top-8)",
+            "hidden": H, "inter": I, "n_routed": E, "n_shared": 1, "top_k": K, "bsz": 1,
+            "weights": "fp9 body+sign planes, resident in HBM",
+            "layer_hbm_gbps": gbps,
+            "layer_hbm_frac": gbps / HBM_PEAK_GBPS,
+            "us_per_layer_p10_p50_p90": [r1["p10_us"], r1["p50_us"], r1["p90_us"]],
+            "bsz2_tokens_per_s": r2["tokens_per_s"] if r2 else None,
+            "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
+            "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_gate_up (gate/up GEMVs + SwiGLU)",
+            "achieved": gu_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gu_gbps / HBM_PEAK_GBPS,
+            "avg_launch_us": r1["gate_up_us"],
+            "bytes_per_launch": r1["bytes_gate_up"],
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,27 @@
+"""fp9 routed-expert MoE FFN for MI355X (gfx950).
+
+The compute path lives in libduckmoe.so (HIP kernels behind the C ABI declared
+in include/duckmoe.h); this package is its ctypes binding plus the seeded
+synthetic-input generator.  Build the library with
+`python -m bit_moe_expert_fp9_amd.build`.
+"""
+
+from .duckmoe import (  # noqa: F401
+    DuckMoeError,
+    EXPORTS,
+    LIB_PATH,
+    Layer,
+    LayerStruct,
+    decode_fp9,
+    expert_ffn,
+    gemv_fp9,
+    lib,
+    moe_down,
+    moe_gate_up,
+    moe_layer,
+    moe_plan,
+    quantize_fp9,
+    status,
+    strerror,
+)
+from . import synth  # noqa: F401

@@ -1,0 +1,688 @@
+// duckmoe.hip - device side of libduckmoe: fp9 routed-expert MoE FFN on gfx950.
+//
+// What is computed (sources cited by page title and section):
+//  * fp9 decode and split storage: duck-llm memoir page "一鸭三吃：我把评测鸭
+//    变成了满血 DeepSeek-V3.2 推理系统", section "在只有 AVX2 的 N100 上，我先做
+//    出了单核 MLP fp9" (see fp9_device.h).
+//  * expert FFN of the routed layer, out_t = shared(x_t) + sum_i w_ti expert_i(x_t),
+//    top_k = 8 routed experts per token, bsz 1-2: chapter page "第 9 章 MTP1
+//    dual-lane overlap", section 9.2 "两条路线的判断"; the expert weights are the
+//    part the memoir page's section "真正埋下伏笔的是内存；R1 之后，问题第一次被
+//    改写" moves off the GPU.
+//  * shard partials: the memoir page's sections "真正难的不是把参数塞下，而是
+//    通信" (tensor parallel) and "16 tok/s 之后：一段没有跑通的路" (per-box
+//    partials, host reduce); ds4 glossary page "张量并行（Tensor Parallelism,
+//    TP）", section "形态一：Mac-to-Mac 张量并行（RDMA）" (f32 partials).
+//
+// How it maps to CDNA (gfx950): the layer is a weight-streaming GEMV (about 2
+// flops per weight byte at bsz 1), so it is HBM-bound and uses the vector ALUs,
+// not MFMA.  Two launches per layer:
+//   k_gate_up: one workgroup per (expert slot, block of intermediate rows).
+//     Each wave owns P (gate row, up row) pairs and walks the hidden dimension
+//     in 1024-weight chunks: every lane loads 16 body bytes (one 128-bit load)
+//     and 2 sign bytes per row, decodes them in registers and FMAs them against
+//     the activation slice it reads from LDS (x is staged there once per
+//     workgroup).  At the end the wave sums its lanes with DPP, applies SwiGLU
+//     and the routing weight, and stores h' = w * silu(g) * v (f32) in the
+//     workspace.
+//   k_down: one workgroup per block of R output rows.  Its waves split the
+//     (expert slot, 1024-wide chunk of the intermediate dimension) items, each
+//     wave streaming the R down rows of its items and FMAing them against h'.
+//     Because the routing weight is already folded into h', the weighted
+//     combine is part of the same dot product.  Lanes are reduced in groups
+//     whose width matches the shard slice, and the waves' partial sums are
+//     added in LDS in a fixed order: every output element is written once, no
+//     atomics, bit-reproducible run to run.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/duckmoe.h"
+#include "fp9_device.h"
+
+namespace duckmoe {
+namespace {
+
+constexpr int kMaxT = DUCKMOE_MAX_TOKENS;
+constexpr int kMaxIds = DUCKMOE_MAX_IDS;
+constexpr int kMaxSlots = kMaxIds + 1;
+constexpr int kMaxWords = DUCKMOE_MAX_ROUTED / 32;
+constexpr int kChunk = 1024;          // weights per wave-row step: 64 lanes x 16
+constexpr size_t kHdrBytes = 4096;    // workspace header (status, plan)
+constexpr int kXLdsBudget = 65536;    // bytes of LDS for the staged activations
+
+// Workspace header, written by block (0,0) of the gate/up launch.
+struct WsHeader {
+  int32_t status;
+  int32_t n_slots;
+};
+
+struct LayerArgs {
+  int H, I, n_routed, top_k, T, n_shards;
+  const uint8_t *gu_body, *gu_sign, *dn_body, *dn_sign;
+  const float *x;
+  const int32_t *ids;  // nullptr: single-expert mode
+  const float *w;
+  int single_expert;
+  float *out;
+  WsHeader *hdr;
+  float *hbuf;         // h' [slot][t][I]
+};
+
+// ----------------------------------------------------------------- plan ----
+// Expert-selection plan, built by every workgroup from the <= 64 routed ids:
+// slots 0..n-1 are the ascending distinct valid ids, slot n is the shared
+// expert (index n_routed, weight 1).  w[slot][t] is token t's routing weight
+// for the slot (summed over repeats, 0 if the token does not use it).
+struct PlanLds {
+  int n_slots;
+  int status;
+  int expert[kMaxSlots];
+  float w[kMaxSlots][kMaxT];
+  uint32_t bitmap[kMaxWords];
+  int prefix[kMaxWords];
+};
+
+__device__ void build_plan(PlanLds &P, const LayerArgs &a) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (a.ids == nullptr) {
+    if (tid == 0) {
+      P.n_slots = 1;
+      P.status = 0;
+      P.expert[0] = a.single_expert;
+    }
+    if (tid < kMaxT) P.w[0][tid] = 1.0f;
+    __syncthreads();
+    return;
+  }
+  const int N = a.T * a.top_k;
+  const int nwords = (a.n_routed + 31) >> 5;
+  for (int i = tid; i < nwords; i += nt) P.bitmap[i] = 0u;
+  for (int i = tid; i < kMaxSlots * kMaxT; i += nt) (&P.w[0][0])[i] = 0.0f;
+  if (tid == 0) P.status = 0;
+  __syncthreads();
+
+  int id = -1;
+  bool valid = false;
+  int tok = 0, base = 0;
+  if (tid < N) {
+    id = a.ids[tid];
+    valid = id >= 0 && id < a.n_routed;
+    tok = tid / a.top_k;
+    base = tok * a.top_k;
+    int st = 0;
+    if (!valid) {
+      st |= DUCKMOE_STATUS_BAD_ID;
+    } else {
+      atomicOr(&P.bitmap[id >> 5], 1u << (id & 31));
+      for (int j = base; j < tid; ++j)
+        if (a.ids[j] == id) st |= DUCKMOE_STATUS_DUP_ID;
+    }
+    if (st) atomicOr(&P.status, st);
+  }
+  __syncthreads();
+  for (int i = tid; i < nwords; i += nt) P.prefix[i] = __popc(P.bitmap[i]);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nwords; ++i) {
+      const int c = P.prefix[i];
+      P.prefix[i] = run;
+      run += c;
+    }
+    P.n_slots = run + 1;
+    P.expert[run] = a.n_routed;
+  }
+  __syncthreads();
+  if (valid) {
+    const int wd = id >> 5;
+    const int slot = P.prefix[wd] + __popc(P.bitmap[wd] & ((1u << (id & 31)) - 1u));
+    P.expert[slot] = id;  // every lane holding this id writes the same value
+    bool first = true;
+    for (int j = base; j < tid; ++j)
+      if (a.ids[j] == id) first = false;
+    if (first && a.w != nullptr) {
+      float s = 0.0f;
+      for (int j = base; j < base + a.top_k; ++j)
+        if (a.ids[j] == id) s += a.w[j];
+      P.w[slot][tok] = s;
+    }
+  }
+  if (tid < a.T) P.w[P.n_slots - 1][tid] = 1.0f;
+  __syncthreads();
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------- gate / up ----
+// grid = (ceil(I / (P*WA)), max slots), block = WA waves.
+// Dynamic LDS: T * cpp * 1024 floats of activations (cpp chunks per phase).
+template <int T, int P, int WA>
+__global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const int cpp) {
+  __shared__ PlanLds plan;
+  extern __shared__ float4 xs4[];
+  build_plan(plan, a);
+  const int slot = blockIdx.y;
+  if (slot >= plan.n_slots) return;  // whole workgroup
+  if (blockIdx.x == 0 && slot == 0 && threadIdx.x == 0) {
+    a.hdr->status = plan.status;
+    a.hdr->n_slots = plan.n_slots;
+  }
+  const int H = a.H, I = a.I;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+  const uint32_t mat = (uint32_t)I * (uint32_t)H;  // bytes of one body matrix
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
+  const int i0 = (blockIdx.x * WA + wave) * P;
+  const int nc = (H + kChunk - 1) / kChunk;
+
+  // per-row lane offsets into the gate (g = 0) and up (g = 1) halves
+  uint32_t ob[2][P], os[2][P];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int row = i0 + p;
+      const uint32_t r = (uint32_t)g * I + row;
+      ob[g][p] = row < I ? r * H + lane * 16 : kOutOfRange;
+      os[g][p] = row < I ? r * (H / 8) + lane * 2 : kOutOfRange;
+    }
+
+  float acc[2][P][T][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
+
+  for (int c0 = 0; c0 < nc; c0 += cpp) {
+    const int cn = min(cpp, nc - c0);
+    const int per_t = cn * (kChunk / 4);  // float4 per token in this phase
+    __syncthreads();
+    for (int q = threadIdx.x; q < T * per_t; q += WA * 64) {
+      const int t = q / per_t, r = q - t * per_t;
+      const int k = c0 * kChunk + r * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < H) v = *reinterpret_cast<const float4 *>(a.x + (size_t)t * H + k);
+      xs4[q] = v;
+    }
+    __syncthreads();
+    for (int cc = 0; cc < cn; ++cc) {
+      const uint32_t kc = (uint32_t)(c0 + cc) * kChunk;
+      const bool kv = kc + lane * 16 < (uint32_t)H;
+      uint4 d[2][P];
+      uint32_t s[2][P];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          d[g][p] = buf_load16(rb, kv ? ob[g][p] + kc : kOutOfRange);
+          s[g][p] = buf_load2(rs, kv ? os[g][p] + kc / 8 : kOutOfRange);
+        }
+      float xv[T][16];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4 *src = xs4 + t * per_t + cc * (kChunk / 4) + lane * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = src[j];
+          xv[t][4 * j + 0] = v.x;
+          xv[t][4 * j + 1] = v.y;
+          xv[t][4 * j + 2] = v.z;
+          xv[t][4 * j + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          h2_t h[8];
+          fp9_decode16(d[g][p], s[g][p], h);
+#pragma unroll
+          for (int t = 0; t < T; ++t) fma16(h, xv[t], acc[g][p][t][0], acc[g][p][t][1]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int row = i0 + p;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float gsum = wave_sum(acc[0][p][t][0] + acc[0][p][t][1]);
+      const float vsum = wave_sum(acc[1][p][t][0] + acc[1][p][t][1]);
+      if (lane == 0 && row < I) {
+        const float wt = plan.w[slot][t];
+        const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gsum) * vsum);
+        a.hbuf[((size_t)slot * T + t) * I + row] = hv;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down ----
+// grid = ceil(H / R), block = WB waves.  Wave w handles chunk c = w % nc of the
+// intermediate dimension for slots w / nc, w / nc + WB / nc, ...
+// Dynamic LDS: WB * R * T * 16 floats (lane-group partial sums).
+template <int G>
+__device__ __forceinline__ void store_groups(float v, float *dst, int lane) {
+  v = group_sum<G>(v);
+  if ((lane & (G - 1)) == G - 1) dst[lane / G] = v;
+}
+
+template <int T, int R, int WB>
+__global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G) {
+  __shared__ PlanLds plan;
+  extern __shared__ float red[];
+  build_plan(plan, a);
+  const int H = a.H, I = a.I;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = blockIdx.x * R;
+  const int nc = (I + kChunk - 1) / kChunk;
+  const int per_c = WB / nc;  // waves per chunk
+  const int S = plan.n_slots;
+  const uint32_t mat = (uint32_t)H * (uint32_t)I;
+  const uint32_t hbytes = (uint32_t)(S * T * I) * 4u;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, hbytes);
+
+  float acc[R][T][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[r][t][0] = acc[r][t][1] = 0.0f;
+
+  if (wave < nc * per_c) {
+    const int c = wave % nc;
+    const uint32_t k = (uint32_t)c * kChunk + lane * 16;
+    const bool kv = k < (uint32_t)I;
+    uint32_t ob[R], os[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      ob[r] = (kv && row < H) ? (uint32_t)row * I + k : kOutOfRange;
+      os[r] = (kv && row < H) ? (uint32_t)row * (I / 8) + k / 8 : kOutOfRange;
+    }
+    for (int slot = wave / nc; slot < S; slot += per_c) {
+      const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
+      uint4 d[R];
+      uint32_t s[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        d[r] = buf_load16(rb, ob[r]);
+        s[r] = buf_load2(rs, os[r]);
+      }
+      float hv[T][16];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t off = kv ? ((uint32_t)(slot * T + t) * I + k) * 4u : kOutOfRange;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = buf_loadf4(rh, off + 16 * j);
+          hv[t][4 * j + 0] = v.x;
+          hv[t][4 * j + 1] = v.y;
+          hv[t][4 * j + 2] = v.z;
+          hv[t][4 * j + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        h2_t h[8];
+        fp9_decode16(d[r], s[r], h);
+#pragma unroll
+        for (int t = 0; t < T; ++t) fma16(h, hv[t], acc[r][t][0], acc[r][t][1]);
+      }
+    }
+  }
+
+  // lane groups of G lanes -> 64/G partial sums per (wave, row, token)
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float *dst = red + ((wave * R + r) * T + t) * 16;
+      const float v = acc[r][t][0] + acc[r][t][1];
+      switch (G) {
+        case 4: store_groups<4>(v, dst, lane); break;
+        case 8: store_groups<8>(v, dst, lane); break;
+        case 16: store_groups<16>(v, dst, lane); break;
+        case 32: store_groups<32>(v, dst, lane); break;
+        default: store_groups<64>(v, dst, lane); break;
+      }
+    }
+  __syncthreads();
+
+  // combine: output (shard, t, row).  Slice width = I / n_shards.
+  const int ns = a.n_shards;
+  const int width = I / ns;
+  for (int q = threadIdx.x; q < ns * T * R; q += WB * 64) {
+    const int shard = q / (T * R);
+    const int rem = q - shard * (T * R);
+    const int t = rem / R, r = rem - t * R;
+    const int row = row0 + r;
+    if (row >= H) continue;
+    int c_lo, c_hi, grp;
+    if (ns == 1) {
+      c_lo = 0; c_hi = nc; grp = 0;
+    } else if (width >= kChunk) {
+      c_lo = shard * (width / kChunk); c_hi = c_lo + width / kChunk; grp = 0;
+    } else {
+      c_lo = (shard * width) / kChunk; c_hi = c_lo + 1;
+      grp = ((shard * width) % kChunk) / (G * 16);
+    }
+    float sum = 0.0f;
+    for (int w = 0; w < nc * per_c; ++w) {
+      const int c = w % nc;
+      if (c >= c_lo && c < c_hi) sum += red[((w * R + r) * T + t) * 16 + grp];
+    }
+    a.out[((size_t)shard * T + t) * H + row] = sum;
+  }
+}
+
+// ------------------------------------------------------ building blocks ----
+__global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ body,
+                                                const uint8_t *__restrict__ sign, int64_t n,
+                                                float *__restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t groups = (n + 7) / 8;
+  if (g >= groups) return;
+  const int64_t base = g * 8;
+  const int cnt = (int)min<int64_t>(8, n - base);
+  uint32_t dw[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < cnt) dw[i >> 2] |= (uint32_t)body[base + i] << (8 * (i & 3));
+  h2_t h[4];
+  fp9_decode8(dw[0], dw[1], sign[g], h);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < cnt) out[base + i] = (i & 1) ? (float)h[i >> 1].y : (float)h[i >> 1].x;
+}
+
+// y = W x: each wave owns R rows, lanes stride over groups of 8 weights.
+template <int R>
+__global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ body,
+                                              const uint8_t *__restrict__ sign, int rows,
+                                              int cols, const float *__restrict__ x,
+                                              float *__restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * R;
+  if (row0 >= rows) return;  // whole wave
+  const int ng = cols / 8;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int g = lane; g < ng; g += 64) {
+    const float4 xa = *reinterpret_cast<const float4 *>(x + 8 * g);
+    const float4 xb = *reinterpret_cast<const float4 *>(x + 8 * g + 4);
+    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      if (row < rows) {
+        const uint2 d = *reinterpret_cast<const uint2 *>(body + (size_t)row * cols + 8 * g);
+        const uint32_t s = sign[(size_t)row * ng + g];
+        h2_t h[4];
+        fp9_decode8(d.x, d.y, s, h);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc[r] = __builtin_fmaf((float)h[p].x, xv[2 * p], acc[r]);
+          acc[r] = __builtin_fmaf((float)h[p].y, xv[2 * p + 1], acc[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < rows) y[row0 + r] = v;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_plan(const LayerArgs a, int32_t *uniq, int32_t *n_slots) {
+  __shared__ PlanLds plan;
+  build_plan(plan, a);
+  for (int s = threadIdx.x; s < plan.n_slots; s += blockDim.x) uniq[s] = plan.expert[s];
+  if (threadIdx.x == 0) *n_slots = plan.n_slots;
+}
+
+// ------------------------------------------------------------ host side ----
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+int check_layer(const duckmoe_layer *L) {
+  if (!L || !L->gu_body || !L->gu_sign || !L->dn_body || !L->dn_sign) return DUCKMOE_EINVAL;
+  if (L->hidden < 16 || L->hidden % 16 || L->inter < 16 || L->inter % 16 || L->inter > 4096 ||
+      L->top_k < 1 || L->n_routed < 1 || L->n_routed > DUCKMOE_MAX_ROUTED)
+    return DUCKMOE_ESHAPE;
+  // one buffer descriptor spans an expert's gate+up bodies: 2*H*I < 2^31
+  if (2ll * L->hidden * L->inter > 0x7fffffffll) return DUCKMOE_ESHAPE;
+  if (!aligned(L->gu_body, 16) || !aligned(L->dn_body, 16) || !aligned(L->gu_sign, 2) ||
+      !aligned(L->dn_sign, 2))
+    return DUCKMOE_EINVAL;
+  return DUCKMOE_OK;
+}
+
+int check_shards(int I, int ns) {
+  if (ns < 1 || I % ns) return DUCKMOE_ESHAPE;
+  if (ns == 1) return DUCKMOE_OK;
+  const int w = I / ns;
+  if (w % kChunk == 0) return DUCKMOE_OK;
+  if (w >= 64 && w <= kChunk && (w & (w - 1)) == 0) return DUCKMOE_OK;
+  return DUCKMOE_ESHAPE;
+}
+
+int group_width(int I, int ns) {
+  if (ns == 1) return 64;
+  const int w = I / ns;
+  return w >= kChunk ? 64 : w / 16;
+}
+
+size_t hbuf_slots(const duckmoe_layer *L, int T, bool single) {
+  return single ? 1 : (size_t)T * L->top_k + 1;
+}
+
+size_t ws_need(const duckmoe_layer *L, int T, bool single) {
+  return kHdrBytes + hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
+}
+
+constexpr int kWA = 4;   // waves per gate/up workgroup
+constexpr int kWB = 6;   // waves per down workgroup
+
+template <int T>
+constexpr int pairs_per_wave() { return T <= 4 ? 4 : 2; }
+template <int T>
+constexpr int down_rows() { return T <= 2 ? 16 : (T <= 4 ? 8 : 4); }
+
+template <int T>
+hipError_t launch_gate_up_t(const LayerArgs &a, int slots, hipStream_t st) {
+  constexpr int P = pairs_per_wave<T>();
+  const int nc = (a.H + kChunk - 1) / kChunk;
+  int cpp = kXLdsBudget / (T * kChunk * (int)sizeof(float));
+  cpp = max(1, min(cpp, nc));
+  const size_t lds = (size_t)T * cpp * kChunk * sizeof(float);
+  const dim3 grid((a.I + P * kWA - 1) / (P * kWA), slots);
+  hipLaunchKernelGGL((k_gate_up<T, P, kWA>), grid, dim3(kWA * 64), lds, st, a, cpp);
+  return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
+  constexpr int R = down_rows<T>();
+  const size_t lds = (size_t)kWB * R * T * 16 * sizeof(float);
+  const dim3 grid((a.H + R - 1) / R);
+  hipLaunchKernelGGL((k_down<T, R, kWB>), grid, dim3(kWB * 64), lds, st, a,
+                     group_width(a.I, a.n_shards));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const LayerArgs &a, int slots, hipStream_t st) {
+  switch (a.T) {
+    case 1: return launch_gate_up_t<1>(a, slots, st);
+    case 2: return launch_gate_up_t<2>(a, slots, st);
+    case 3: return launch_gate_up_t<3>(a, slots, st);
+    case 4: return launch_gate_up_t<4>(a, slots, st);
+    case 5: return launch_gate_up_t<5>(a, slots, st);
+    case 6: return launch_gate_up_t<6>(a, slots, st);
+    case 7: return launch_gate_up_t<7>(a, slots, st);
+    default: return launch_gate_up_t<8>(a, slots, st);
+  }
+}
+
+hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
+  switch (a.T) {
+    case 1: return launch_down_t<1>(a, st);
+    case 2: return launch_down_t<2>(a, st);
+    case 3: return launch_down_t<3>(a, st);
+    case 4: return launch_down_t<4>(a, st);
+    case 5: return launch_down_t<5>(a, st);
+    case 6: return launch_down_t<6>(a, st);
+    case 7: return launch_down_t<7>(a, st);
+    default: return launch_down_t<8>(a, st);
+  }
+}
+
+enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
+
+// Shared argument checks and dispatch of the layer entry points.
+int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const float *w,
+              int single_expert, int32_t T, float *out, int32_t n_shards, void *ws,
+              size_t ws_bytes, hipStream_t stream, int stages) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  const bool single = ids == nullptr;
+  if (T < 1 || T > kMaxT) return DUCKMOE_EINVAL;
+  if (!single && !w) return DUCKMOE_EINVAL;
+  if (!single && T * L->top_k > kMaxIds) return DUCKMOE_ESHAPE;
+  if (single && (single_expert < 0 || single_expert > L->n_routed)) return DUCKMOE_EINVAL;
+  if (!x || !out || !ws) return DUCKMOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(out, 4) || !aligned(ws, 256)) return DUCKMOE_EINVAL;
+  rc = check_shards(L->inter, n_shards);
+  if (rc) return rc;
+  if (ws_bytes < ws_need(L, T, single)) return DUCKMOE_EWORKSPACE;
+
+  LayerArgs a;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.n_routed = L->n_routed;
+  a.top_k = L->top_k;
+  a.T = T;
+  a.n_shards = n_shards;
+  a.gu_body = L->gu_body;
+  a.gu_sign = L->gu_sign;
+  a.dn_body = L->dn_body;
+  a.dn_sign = L->dn_sign;
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  a.single_expert = single_expert;
+  a.out = out;
+  a.hdr = reinterpret_cast<WsHeader *>(ws);
+  a.hbuf = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes);
+
+  if (stages & kGateUp) {
+    if (launch_gate_up(a, (int)hbuf_slots(L, T, single), stream) != hipSuccess)
+      return DUCKMOE_EHIP;
+  }
+  if (stages & kDown) {
+    if (launch_down(a, stream) != hipSuccess) return DUCKMOE_EHIP;
+  }
+  return DUCKMOE_OK;
+}
+
+}  // namespace
+}  // namespace duckmoe
+
+using namespace duckmoe;
+
+extern "C" {
+
+size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shards) {
+  if (check_layer(L) || T < 1 || T > kMaxT || T * L->top_k > kMaxIds ||
+      check_shards(L->inter, n_shards))
+    return 0;
+  return ws_need(L, T, false);
+}
+
+int duckmoe_moe_layer(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                      const float *w, int32_t T, float *out, int32_t n_shards, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  if (!ids) return DUCKMOE_EINVAL;
+  return run_layer(L, x, ids, w, 0, T, out, n_shards, ws, ws_bytes, stream, kBoth);
+}
+
+int duckmoe_moe_gate_up(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                        const float *w, int32_t T, float *out, int32_t n_shards, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (!ids) return DUCKMOE_EINVAL;
+  return run_layer(L, x, ids, w, 0, T, out, n_shards, ws, ws_bytes, stream, kGateUp);
+}
+
+int duckmoe_moe_down(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                     const float *w, int32_t T, float *out, int32_t n_shards, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!ids) return DUCKMOE_EINVAL;
+  return run_layer(L, x, ids, w, 0, T, out, n_shards, ws, ws_bytes, stream, kDown);
+}
+
+int duckmoe_expert_ffn(const duckmoe_layer *L, int32_t e, const float *x, int32_t T,
+                       float *out, int32_t n_shards, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return run_layer(L, x, nullptr, nullptr, e, T, out, n_shards, ws, ws_bytes, stream, kBoth);
+}
+
+int duckmoe_status(const void *ws, int32_t *status, hipStream_t stream) {
+  if (!ws || !status) return DUCKMOE_EINVAL;
+  WsHeader h;
+  if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return DUCKMOE_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return DUCKMOE_EHIP;
+  *status = h.status;
+  return DUCKMOE_OK;
+}
+
+int duckmoe_decode_fp9(const uint8_t *body, const uint8_t *sign, int64_t n, float *out,
+                       hipStream_t stream) {
+  if (n < 0 || !body || !sign || !out) return DUCKMOE_EINVAL;
+  if (n == 0) return DUCKMOE_OK;
+  const int64_t groups = (n + 7) / 8;
+  const int64_t blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffff) return DUCKMOE_ESHAPE;
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)blocks), dim3(256), 0, stream, body, sign, n, out);
+  return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+int duckmoe_gemv_fp9(const uint8_t *body, const uint8_t *sign, int32_t rows, int32_t cols,
+                     const float *x, float *y, hipStream_t stream) {
+  if (!body || !sign || !x || !y || rows < 0 || cols < 0) return DUCKMOE_EINVAL;
+  if (cols % 8) return DUCKMOE_ESHAPE;
+  if (!aligned(body, 8) || !aligned(x, 16) || !aligned(y, 4)) return DUCKMOE_EINVAL;
+  if (rows == 0) return DUCKMOE_OK;
+  constexpr int R = 4;
+  const int waves = (rows + R - 1) / R;
+  const int blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((k_gemv<R>), dim3(blocks), dim3(256), 0, stream, body, sign, rows, cols, x,
+                     y);
+  return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+int duckmoe_moe_plan(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_routed,
+                     int32_t *uniq, int32_t *n_slots, hipStream_t stream) {
+  if (!ids || !uniq || !n_slots) return DUCKMOE_EINVAL;
+  if (T < 1 || T > kMaxT || top_k < 1) return DUCKMOE_EINVAL;
+  if (T * top_k > kMaxIds || n_routed < 1 || n_routed > DUCKMOE_MAX_ROUTED)
+    return DUCKMOE_ESHAPE;
+  LayerArgs a = {};
+  a.ids = ids;
+  a.T = T;
+  a.top_k = top_k;
+  a.n_routed = n_routed;
+  a.w = nullptr;  // the slot list needs no weights; build_plan skips them
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, stream, a, uniq, n_slots);
+  return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+}  // extern "C"

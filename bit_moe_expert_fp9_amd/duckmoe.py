@@ -1,0 +1,293 @@
+"""ctypes binding of libduckmoe (include/duckmoe.h).
+
+Argument marshalling only: every step of the path runs inside the library.
+torch provides device memory and the current stream; nothing here computes.
+If the library is not built every call raises: there is no fallback.
+"""
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import synth
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libduckmoe.so")
+
+OK, EINVAL, ESHAPE, ENONFINITE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
+STATUS_BAD_ID, STATUS_DUP_ID = 1, 2
+MAX_TOKENS = 8
+
+_lib = None
+
+
+class DuckMoeError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__("%s: %s (%d)" % (where, strerror(code), code))
+        self.code = code
+
+
+class LayerStruct(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("n_routed", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("gu_body", ctypes.c_void_p),
+        ("gu_sign", ctypes.c_void_p),
+        ("dn_body", ctypes.c_void_p),
+        ("dn_sign", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_LAYER_ARGS = [ctypes.POINTER(LayerStruct), _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P]
+
+_SIGNATURES = {
+    "duckmoe_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "duckmoe_quantize_fp9": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "duckmoe_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
+    "duckmoe_moe_layer": (_LAYER_ARGS, ctypes.c_int),
+    "duckmoe_moe_gate_up": (_LAYER_ARGS, ctypes.c_int),
+    "duckmoe_moe_down": (_LAYER_ARGS, ctypes.c_int),
+    "duckmoe_expert_ffn": ([ctypes.POINTER(LayerStruct), _I32, _P, _I32, _P, _I32, _P, _SZ, _P],
+                           ctypes.c_int),
+    "duckmoe_status": ([_P, ctypes.POINTER(_I32), _P], ctypes.c_int),
+    "duckmoe_decode_fp9": ([_P, _P, _I64, _P, _P], ctypes.c_int),
+    "duckmoe_gemv_fp9": ([_P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "duckmoe_moe_plan": ([_P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+}
+
+EXPORTS = tuple(_SIGNATURES)
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libduckmoe.so is not built: run "
+                               "`python -m bit_moe_expert_fp9_amd.build` (needs hipcc)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def strerror(code):
+    try:
+        return lib().duckmoe_strerror(code).decode()
+    except RuntimeError:
+        return "error %d" % code
+
+
+def _check(rc, where):
+    if rc != OK:
+        raise DuckMoeError(rc, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_device(t, dtype, name):
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s" % (name, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    del torch
+
+
+# ------------------------------------------------------------------ host ----
+
+def quantize_fp9(w, body=None, sign=None):
+    """float32 [rows, cols] -> (body uint8 [rows, cols], sign uint8 [rows, cols/8]).
+
+    Host call into the library; `body`/`sign` may be preallocated numpy arrays.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("quantize_fp9 takes a 2-D array")
+    rows, cols = w.shape
+    if body is None:
+        body = np.empty((rows, cols), dtype=np.uint8)
+    if sign is None:
+        sign = np.empty((rows, max(cols // 8, 0)), dtype=np.uint8)
+    rc = lib().duckmoe_quantize_fp9(w.ctypes.data, rows, cols, body.ctypes.data,
+                                    sign.ctypes.data)
+    _check(rc, "duckmoe_quantize_fp9")
+    return body, sign
+
+
+# ----------------------------------------------------------------- layer ----
+
+class Layer:
+    """One MoE layer's fp9 expert weights resident on the device."""
+
+    def __init__(self, hidden, inter, n_routed, top_k, device="cuda"):
+        import torch
+        self.hidden, self.inter, self.n_routed, self.top_k = hidden, inter, n_routed, top_k
+        E = n_routed + 1
+        mat = inter * hidden
+        self.gu_body = torch.empty(E * 2 * mat, dtype=torch.uint8, device=device)
+        self.gu_sign = torch.empty(E * 2 * mat // 8, dtype=torch.uint8, device=device)
+        self.dn_body = torch.empty(E * mat, dtype=torch.uint8, device=device)
+        self.dn_sign = torch.empty(E * mat // 8, dtype=torch.uint8, device=device)
+        self.struct = LayerStruct(hidden, inter, n_routed, top_k, self.gu_body.data_ptr(),
+                                  self.gu_sign.data_ptr(), self.dn_body.data_ptr(),
+                                  self.dn_sign.data_ptr())
+
+    @property
+    def n_experts(self):
+        return self.n_routed + 1
+
+    def expert_bytes(self):
+        """fp9 bytes one expert streams (3 matrices, body + sign)."""
+        return 3 * self.inter * self.hidden * 9 // 8
+
+    def set_expert(self, e, gate, up, down):
+        """Quantize float32 matrices (gate/up [I,H], down [H,I]) into expert e."""
+        import torch
+        H, I = self.hidden, self.inter
+        mat = I * H
+        gb, gs = quantize_fp9(np.concatenate([gate, up], axis=0))
+        db, dsn = quantize_fp9(down)
+        self.gu_body[e * 2 * mat:(e + 1) * 2 * mat].copy_(torch.from_numpy(gb.reshape(-1)))
+        self.gu_sign[e * 2 * mat // 8:(e + 1) * 2 * mat // 8].copy_(torch.from_numpy(gs.reshape(-1)))
+        self.dn_body[e * mat:(e + 1) * mat].copy_(torch.from_numpy(db.reshape(-1)))
+        self.dn_sign[e * mat // 8:(e + 1) * mat // 8].copy_(torch.from_numpy(dsn.reshape(-1)))
+
+    def fill_synthetic(self, seed, workload, layer, threads=None):
+        """Draw every expert from synth.weights and upload it (threaded)."""
+        H, I = self.hidden, self.inter
+
+        def one(e):
+            gate = synth.weights(seed, workload, layer, e, synth.GATE, (I, H))
+            up = synth.weights(seed, workload, layer, e, synth.UP, (I, H))
+            down = synth.weights(seed, workload, layer, e, synth.DOWN, (H, I))
+            self.set_expert(e, gate, up, down)
+
+        if threads is None:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            list(ex.map(one, range(self.n_experts)))
+        import torch
+        torch.cuda.synchronize()
+        return self
+
+    def workspace_bytes(self, T, n_shards=1):
+        n = lib().duckmoe_workspace_bytes(ctypes.byref(self.struct), T, n_shards)
+        if n == 0:
+            raise DuckMoeError(EINVAL, "duckmoe_workspace_bytes")
+        return n
+
+    def workspace(self, T, n_shards=1):
+        import torch
+        return torch.empty(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
+                           device=self.gu_body.device)
+
+
+def _layer_call(fname, layer, x, ids, w, out, n_shards, ws, stream):
+    import torch
+    T = x.shape[0]
+    _need_device(x, torch.float32, "x")
+    if ids is not None:
+        _need_device(ids, torch.int32, "ids")
+        _need_device(w, torch.float32, "w")
+    if out is None:
+        shape = (T, layer.hidden) if n_shards == 1 else (n_shards, T, layer.hidden)
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = layer.workspace(T, n_shards)
+    rc = getattr(lib(), fname)(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w), T,
+                               _ptr(out), n_shards, _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, fname)
+    return out
+
+
+def moe_layer(layer, x, ids, w, out=None, n_shards=1, ws=None, stream=None):
+    """out = shared(x) + sum_i w[:, i] * expert_{ids[:, i]}(x); device tensors."""
+    return _layer_call("duckmoe_moe_layer", layer, x, ids, w, out, n_shards, ws, stream)
+
+
+def moe_gate_up(layer, x, ids, w, ws, out=None, n_shards=1, stream=None):
+    return _layer_call("duckmoe_moe_gate_up", layer, x, ids, w, out, n_shards, ws, stream)
+
+
+def moe_down(layer, x, ids, w, ws, out=None, n_shards=1, stream=None):
+    return _layer_call("duckmoe_moe_down", layer, x, ids, w, out, n_shards, ws, stream)
+
+
+def expert_ffn(layer, e, x, out=None, n_shards=1, ws=None, stream=None):
+    import torch
+    T = x.shape[0]
+    _need_device(x, torch.float32, "x")
+    if out is None:
+        shape = (T, layer.hidden) if n_shards == 1 else (n_shards, T, layer.hidden)
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = layer.workspace(T, n_shards)
+    rc = lib().duckmoe_expert_ffn(ctypes.byref(layer.struct), e, _ptr(x), T, _ptr(out),
+                                  n_shards, _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "duckmoe_expert_ffn")
+    return out
+
+
+def status(ws, stream=None):
+    st = _I32(0)
+    _check(lib().duckmoe_status(_ptr(ws), ctypes.byref(st), _stream(stream)), "duckmoe_status")
+    return st.value
+
+
+# --------------------------------------------------------- building blocks ----
+
+def decode_fp9(body, sign, n=None, out=None, stream=None):
+    """Device decode of fp9 planes to float32 (test export)."""
+    import torch
+    n = body.numel() if n is None else n
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=body.device)
+    _check(lib().duckmoe_decode_fp9(_ptr(body), _ptr(sign), n, _ptr(out), _stream(stream)),
+           "duckmoe_decode_fp9")
+    return out
+
+
+def gemv_fp9(body, sign, x, out=None, stream=None):
+    """y = W x with W in fp9 planes body [rows, cols], sign [rows, cols/8]."""
+    import torch
+    rows, cols = body.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=body.device)
+    _check(lib().duckmoe_gemv_fp9(_ptr(body), _ptr(sign), rows, cols, _ptr(x), _ptr(out),
+                                  _stream(stream)), "duckmoe_gemv_fp9")
+    return out
+
+
+def moe_plan(ids, n_routed, stream=None):
+    """Device expert-selection plan -> list of expert indices (shared last)."""
+    import torch
+    T, k = ids.shape
+    uniq = torch.full((T * k + 1,), -1, dtype=torch.int32, device=ids.device)
+    n = torch.zeros(1, dtype=torch.int32, device=ids.device)
+    _check(lib().duckmoe_moe_plan(_ptr(ids), T, k, n_routed, _ptr(uniq), _ptr(n),
+                                  _stream(stream)), "duckmoe_moe_plan")
+    cnt = int(n.item())
+    return uniq[:cnt].cpu().tolist()

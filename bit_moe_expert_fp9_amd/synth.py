@@ -1,0 +1,56 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle runs.
+
+This module draws random numbers and nothing else: it holds none of the
+method's arithmetic (no fp9 rounding, no decode, no GEMV).  Both the library
+path and the oracle take its float32 arrays and quantize them on their own.
+
+Recipe (the pages measure on trained DeepSeek-V3.2 weights and their own
+prompts, neither available; these draws stand in, with the layer's shapes):
+  * weights: N(0, 0.02) float32, one independent stream per
+    (seed, workload, layer, expert, matrix), matrix 0 = gate, 1 = up, 2 = down;
+  * activations: N(0, 1) float32 per (seed, workload, layer, step);
+  * routing per token: 8 (top_k) distinct ids drawn uniformly from the routed
+    experts, weights = softmax of top_k N(0, 1) draws, per
+    (seed, workload, layer, step).
+Every stream is numpy's PCG64 seeded by SeedSequence of the tuple above.
+"""
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+GATE, UP, DOWN = 0, 1, 2
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def weights(seed, workload, layer, expert, matrix, shape, out=None):
+    """N(0, 0.02) float32 of the given shape (optionally written into `out`)."""
+    rng = _rng(seed, workload, layer, expert, matrix, 0)
+    if out is None:
+        out = np.empty(shape, dtype=np.float32)
+    rng.standard_normal(out=out, dtype=np.float32)
+    out *= np.float32(WEIGHT_STD)
+    return out
+
+
+def activations(seed, workload, layer, step, T, hidden):
+    """x [T, hidden] ~ N(0, 1), float32."""
+    rng = _rng(seed, workload, layer, step, 1)
+    return rng.standard_normal((T, hidden), dtype=np.float32)
+
+
+def routing(seed, workload, layer, step, T, n_routed, top_k):
+    """(ids int32 [T, top_k], w float32 [T, top_k]) for one decode step."""
+    rng = _rng(seed, workload, layer, step, 2)
+    ids = np.stack([rng.choice(n_routed, size=top_k, replace=False) for _ in range(T)])
+    z = rng.standard_normal((T, top_k))
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w.astype(np.float32)
+
+
+def expert_shapes(hidden, inter):
+    """(gate, up, down) matrix shapes of one expert."""
+    return (inter, hidden), (inter, hidden), (hidden, inter)

@@ -1,0 +1,200 @@
+/*
+ * duckmoe.h - C ABI of libduckmoe: the fp9 routed-expert MoE FFN on gfx950.
+ *
+ * Sources (cited by page title and section):
+ *  [fp9]   duck-llm memoir page "一鸭三吃：我把评测鸭变成了满血 DeepSeek-V3.2
+ *          推理系统", section "在只有 AVX2 的 N100 上，我先做出了单核 MLP fp9":
+ *          9-bit layout figure (sign bit 8, exponent bits 7..3 with bias 15,
+ *          mantissa bits 2..0), body byte + packed sign bitplane storage
+ *          (8 weights in 9 bytes), decode by placing the bits into fp16.
+ *  [afd]   same page, section "真正埋下伏笔的是内存；R1 之后，问题第一次被改写":
+ *          the FFN/MoE expert weights are the part held outside the GPU.
+ *  [tp]    same page, section "真正难的不是把参数塞下，而是通信": tensor
+ *          parallelism is the split that cuts per-token latency at bsz 1;
+ *          section "先用 Qwen3 练级，再让 Qwen3.5 充当高压试炼场": slices
+ *          narrower than 128 (multiple_of 64/32).
+ *  [brk]   same page, section "16 tok/s 之后：一段没有跑通的路": MoE forward
+ *          breakdown (prepare / send / per-box compute / fetch / host reduce).
+ *  [route] chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2
+ *          "两条路线的判断": 8 routed experts per token (top_k = 8); the sets of
+ *          two tokens barely overlap, so bsz 2 reads about twice the weights.
+ *  [f32]   ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
+ *          "形态一：Mac-to-Mac 张量并行（RDMA）": TP partial sums travel as f32.
+ *
+ * Conventions shared by every entry point:
+ *  - Return 0 (DUCKMOE_OK) or a negative DUCKMOE_E* code; nothing throws.
+ *  - Argument errors are detected on the host and returned before anything is
+ *    launched; no output is written then.
+ *  - Device entry points are asynchronous on the given stream (0 = the null
+ *    stream).  A device fault surfaces at the caller's next synchronisation.
+ *  - All memory is caller-owned.  The library allocates nothing and keeps no
+ *    mutable global state, so calls on different streams may run concurrently
+ *    as long as they use different workspaces and outputs.
+ *  - Device pointers must satisfy the alignment stated for them
+ *    (DUCKMOE_EINVAL otherwise).
+ */
+#ifndef DUCKMOE_H
+#define DUCKMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUCKMOE_OK          0
+#define DUCKMOE_EINVAL     -1  /* null/misaligned pointer, T out of [1,8], bad index   */
+#define DUCKMOE_ESHAPE     -2  /* a size the kernels do not support (see each call)    */
+#define DUCKMOE_ENONFINITE -3  /* NaN given to the quantizer                           */
+#define DUCKMOE_EWORKSPACE -4  /* ws_bytes < duckmoe_workspace_bytes(...)              */
+#define DUCKMOE_EHIP       -5  /* the HIP runtime refused a launch or a copy           */
+
+/* Bits of the device status word (duckmoe_status). */
+#define DUCKMOE_STATUS_BAD_ID  1  /* a routed id outside [0, n_routed): entry skipped   */
+#define DUCKMOE_STATUS_DUP_ID  2  /* a token lists an id twice: its weights were added  */
+
+#define DUCKMOE_MAX_TOKENS 8      /* T, tokens per call                                 */
+#define DUCKMOE_MAX_IDS    64     /* T * top_k                                          */
+#define DUCKMOE_MAX_ROUTED 8192   /* n_routed                                           */
+
+/*
+ * One MoE layer's expert weights, resident in device memory, in the [fp9]
+ * split storage.  Expert index n_routed is the shared expert.  H = hidden,
+ * I = inter.  Rows are row-major along the contraction dimension:
+ *   gu_body [n_routed+1][2][I][H]    uint8  gate rows (g=0) then up rows (g=1)
+ *   gu_sign [n_routed+1][2][I][H/8]  uint8  sign byte j of a row: elements 8j..8j+7,
+ *                                            element 8j+i in bit i
+ *   dn_body [n_routed+1][H][I]       uint8  down rows
+ *   dn_sign [n_routed+1][H][I/8]     uint8
+ * Requirements: H and I multiples of 16, 16 <= I <= 4096, H >= 16,
+ * 1 <= top_k, 1 <= n_routed <= DUCKMOE_MAX_ROUTED (DUCKMOE_ESHAPE otherwise);
+ * body pointers 16-byte aligned, sign pointers 2-byte aligned (DUCKMOE_EINVAL).
+ * The struct itself is read on the host during the call only.
+ */
+typedef struct duckmoe_layer {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_routed;
+  int32_t top_k;
+  const uint8_t *gu_body;
+  const uint8_t *gu_sign;
+  const uint8_t *dn_body;
+  const uint8_t *dn_sign;
+} duckmoe_layer;
+
+/* Text for a return code (static storage; never NULL). */
+const char *duckmoe_strerror(int code);
+
+/*
+ * [fp9] Host quantizer and packer, synchronous, HOST pointers.
+ *   w    [rows][cols] float32 (read only)
+ *   body [rows][cols]   uint8  <- bits 7..0 of each code (exponent, mantissa)
+ *   sign [rows][cols/8] uint8  <- sign bits, element 8j+i of a row in bit i of byte j
+ * Rounding: to nearest, ties to even, computed directly from the float32 value
+ * (never via fp16).  |w| >= 61440 and +-inf saturate to +-61440 (exponent 30,
+ * mantissa 7); exponent 31 is never produced; the sign of zero is kept.
+ * Errors: DUCKMOE_EINVAL for null pointers or rows/cols < 0; DUCKMOE_ESHAPE if
+ * cols % 8 != 0; DUCKMOE_ENONFINITE if any element is NaN (the outputs are
+ * then unspecified).  rows or cols == 0 is a no-op.
+ */
+int duckmoe_quantize_fp9(const float *w, int64_t rows, int64_t cols,
+                         uint8_t *body, uint8_t *sign);
+
+/*
+ * Bytes of device workspace duckmoe_expert_ffn / duckmoe_moe_layer need for T
+ * tokens (the same figure covers both).  Returns 0 if the arguments are
+ * invalid.  The workspace holds the expert-selection plan, the status word and
+ * the per-(expert, token) SwiGLU activations (f32).
+ */
+size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shards);
+
+/*
+ * [afd][route][brk] Full routed layer for T tokens (1 <= T <= 8):
+ *   out_t = shared(x_t) + sum_i w[t][i] * expert_{ids[t][i]}(x_t),
+ *   expert(x) = W_down (silu(W_gate x) * (W_up x)),  silu(z) = z / (1 + e^-z).
+ * Only the experts named in ids (their union over the batch) and the shared
+ * expert are read from memory, each once per call.
+ *   x   [T][H]          float32, device, 16-byte aligned
+ *   ids [T][top_k]      int32,   device; ids of one token should be distinct
+ *   w   [T][top_k]      float32, device
+ *   out n_shards == 1:  [T][H] float32, device
+ *       n_shards  > 1:  [n_shards][T][H]: shard r is the same sum restricted to
+ *                       the intermediate slice [r*I/n_shards, (r+1)*I/n_shards)
+ *                       of every expert ([tp][f32]); the shards add up to the
+ *                       n_shards == 1 output.
+ *   n_shards >= 1 must divide I, and the slice width I / n_shards must be a
+ *   multiple of 1024 or a power of two in [64, 1024] (DUCKMOE_ESHAPE otherwise);
+ *   for I = 2048 that is n_shards in {1, 2, 4, 8, 16, 32}.
+ *   ws  device workspace, 256-byte aligned, >= duckmoe_workspace_bytes(L,T,n_shards)
+ * Ids outside [0, n_routed) are skipped and flag DUCKMOE_STATUS_BAD_ID; an id
+ * repeated within a token has its weights added and flags DUCKMOE_STATUS_DUP_ID.
+ */
+int duckmoe_moe_layer(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                      const float *w, int32_t T, float *out, int32_t n_shards,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The two launches duckmoe_moe_layer makes, for callers that time or overlap
+ * them separately.  Same arguments and checks as duckmoe_moe_layer.
+ *   gate_up: plan + gate/up GEMVs + SwiGLU, the routing weight folded in;
+ *            writes only the workspace.
+ *   down:    down GEMVs + routing-weighted combine; reads the workspace the
+ *            gate_up call left (same L, x, ids, w, T, ws) and writes out.
+ */
+int duckmoe_moe_gate_up(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                        const float *w, int32_t T, float *out, int32_t n_shards,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+int duckmoe_moe_down(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                     const float *w, int32_t T, float *out, int32_t n_shards,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One expert e in [0, n_routed] (n_routed = the shared expert) for T tokens,
+ * weight 1: out_t = expert_e(x_t).  Layouts, n_shards and ws as for
+ * duckmoe_moe_layer; DUCKMOE_EINVAL if e is out of range.
+ */
+int duckmoe_expert_ffn(const duckmoe_layer *L, int32_t e, const float *x, int32_t T,
+                       float *out, int32_t n_shards, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * Reads the status word the last layer call on this workspace wrote
+ * (DUCKMOE_STATUS_* bits).  Synchronises `stream` first.  status: host pointer.
+ */
+int duckmoe_status(const void *ws, int32_t *status, hipStream_t stream);
+
+/* ---- building blocks, exported for parity tests ---------------------------- */
+
+/*
+ * [fp9] Decode n codes from the split planes to float32 through the fp16 route
+ * (code << 7 is an fp16 pattern, converted by hardware).
+ *   body [n] uint8, sign [(n+7)/8] uint8, out [n] float32; all device, any alignment.
+ * n == 0 is a no-op; n < 0 or a null pointer -> DUCKMOE_EINVAL.
+ */
+int duckmoe_decode_fp9(const uint8_t *body, const uint8_t *sign, int64_t n,
+                       float *out, hipStream_t stream);
+
+/*
+ * [fp9] y = W x, W [rows][cols] in split storage (body [rows][cols],
+ * sign [rows][cols/8]), x [cols], y [rows] float32; all device.
+ * cols % 8 == 0 (DUCKMOE_ESHAPE); body/x 8-byte aligned (DUCKMOE_EINVAL).
+ */
+int duckmoe_gemv_fp9(const uint8_t *body, const uint8_t *sign, int32_t rows, int32_t cols,
+                     const float *x, float *y, hipStream_t stream);
+
+/*
+ * [route] Expert-selection plan: the ascending distinct valid ids of
+ * ids[T][top_k], then n_routed (the shared expert).
+ *   uniq [T*top_k+1] int32 device <- plan entries (the rest untouched)
+ *   n_slots [1] int32 device      <- number of entries written (distinct + 1)
+ */
+int duckmoe_moe_plan(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_routed,
+                     int32_t *uniq, int32_t *n_slots, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUCKMOE_H */

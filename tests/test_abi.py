@@ -1,0 +1,142 @@
+"""The C ABI loads, exports every declared entry point, and rejects bad
+arguments on the host before launching anything (CPU only: no GPU needed,
+since every call here returns before touching the HIP runtime)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from lib_util import ROOT, ensure_built
+
+import bit_moe_expert_fp9_amd as dm
+from bit_moe_expert_fp9_amd.duckmoe import LayerStruct
+
+HEADER = os.path.join(ROOT, "include", "duckmoe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ensure_built()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(duckmoe_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(dm.EXPORTS) == names
+
+
+def test_strerror(L):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert L.duckmoe_strerror(code)
+    assert dm.strerror(-4) == "workspace too small"
+
+
+def test_quantize_errors(L):
+    w = np.zeros((2, 8), dtype=np.float32)
+    b = np.zeros((2, 8), dtype=np.uint8)
+    s = np.zeros((2, 1), dtype=np.uint8)
+    f = L.duckmoe_quantize_fp9
+    assert f(w.ctypes.data, 2, 8, b.ctypes.data, s.ctypes.data) == 0
+    assert f(w.ctypes.data, 2, 12, b.ctypes.data, s.ctypes.data) == dm.duckmoe.ESHAPE
+    assert f(w.ctypes.data, -1, 8, b.ctypes.data, s.ctypes.data) == dm.duckmoe.EINVAL
+    assert f(None, 2, 8, b.ctypes.data, s.ctypes.data) == dm.duckmoe.EINVAL
+    assert f(None, 0, 8, None, None) == 0
+    w[1, 3] = np.nan
+    assert f(w.ctypes.data, 2, 8, b.ctypes.data, s.ctypes.data) == dm.duckmoe.ENONFINITE
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced
+
+
+def fake_layer(H=7168, I=2048, E=256, k=8):
+    return LayerStruct(H, I, E, k, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_workspace_bytes(L):
+    lay = fake_layer()
+    f = L.duckmoe_workspace_bytes
+    assert f(ctypes.byref(lay), 1, 1) == 4096 + 9 * 1 * 2048 * 4
+    assert f(ctypes.byref(lay), 2, 32) == 4096 + 17 * 2 * 2048 * 4
+    assert f(ctypes.byref(lay), 0, 1) == 0
+    assert f(ctypes.byref(lay), 9, 1) == 0
+    assert f(ctypes.byref(lay), 1, 3) == 0      # 2048 / 3 not integral
+    assert f(ctypes.byref(lay), 1, 64) == 0     # slice of 32 < 64
+    assert f(None, 1, 1) == 0
+
+
+def call_layer(L, lay, x=FAKE, ids=FAKE, w=FAKE, T=1, out=FAKE, ns=1, ws=FAKE,
+               ws_bytes=1 << 30, fn="duckmoe_moe_layer"):
+    return getattr(L, fn)(ctypes.byref(lay) if lay is not None else None, x, ids, w, T, out,
+                          ns, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["duckmoe_moe_layer", "duckmoe_moe_gate_up", "duckmoe_moe_down"])
+def test_layer_argument_errors(L, fn):
+    E = dm.duckmoe
+    lay = fake_layer()
+    c = lambda **kw: call_layer(L, lay, fn=fn, **kw)
+    assert call_layer(L, None, fn=fn) == E.EINVAL
+    assert c(T=0) == E.EINVAL
+    assert c(T=9) == E.EINVAL
+    assert c(ids=None) == E.EINVAL
+    assert c(w=None) == E.EINVAL
+    assert c(x=None) == E.EINVAL
+    assert c(out=None) == E.EINVAL
+    assert c(ws=None) == E.EINVAL
+    assert c(x=FAKE + 4) == E.EINVAL      # x must be 16-byte aligned
+    assert c(ws=FAKE + 16) == E.EINVAL    # workspace 256-byte aligned
+    assert c(ns=3) == E.ESHAPE
+    assert c(ns=64) == E.ESHAPE
+    assert c(ws_bytes=1000) == E.EWORKSPACE
+    big = fake_layer(k=40)
+    assert call_layer(L, big, T=2, fn=fn) == E.ESHAPE   # T * top_k > 64
+    for bad in (fake_layer(H=7160), fake_layer(I=2040), fake_layer(I=8192), fake_layer(E=0),
+                fake_layer(E=9000), fake_layer(k=0)):
+        assert call_layer(L, bad, fn=fn) == E.ESHAPE
+    mis = LayerStruct(7168, 2048, 256, 8, FAKE + 8, FAKE, FAKE, FAKE)
+    assert call_layer(L, mis, fn=fn) == E.EINVAL
+
+
+def test_expert_ffn_errors(L):
+    E = dm.duckmoe
+    lay = fake_layer()
+    f = lambda e, T=1, ns=1, wsb=1 << 30: L.duckmoe_expert_ffn(ctypes.byref(lay), e, FAKE, T, FAKE,
+                                                             ns, FAKE, wsb, None)
+    assert f(-1) == E.EINVAL
+    assert f(257) == E.EINVAL
+    assert f(0, T=0) == E.EINVAL
+    assert f(0, ns=5) == E.ESHAPE
+    assert f(0, wsb=100) == E.EWORKSPACE
+
+
+def test_building_block_errors(L):
+    E = dm.duckmoe
+    assert L.duckmoe_decode_fp9(FAKE, FAKE, -1, FAKE, None) == E.EINVAL
+    assert L.duckmoe_decode_fp9(None, FAKE, 8, FAKE, None) == E.EINVAL
+    assert L.duckmoe_decode_fp9(FAKE, FAKE, 0, FAKE, None) == 0
+    assert L.duckmoe_gemv_fp9(FAKE, FAKE, 4, 12, FAKE, FAKE, None) == E.ESHAPE
+    assert L.duckmoe_gemv_fp9(FAKE, FAKE, 4, 16, FAKE + 4, FAKE, None) == E.EINVAL
+    assert L.duckmoe_gemv_fp9(FAKE, FAKE, 0, 16, FAKE, FAKE, None) == 0
+    assert L.duckmoe_moe_plan(FAKE, 9, 8, 256, FAKE, FAKE, None) == E.EINVAL
+    assert L.duckmoe_moe_plan(FAKE, 8, 9, 256, FAKE, FAKE, None) == E.ESHAPE
+    assert L.duckmoe_moe_plan(None, 1, 8, 256, FAKE, FAKE, None) == E.EINVAL
+    assert L.duckmoe_status(None, None, None) == E.EINVAL
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    from bit_moe_expert_fp9_amd import duckmoe
+    monkeypatch.setattr(duckmoe, "_lib", None)
+    monkeypatch.setattr(duckmoe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        duckmoe.quantize_fp9(np.zeros((1, 8), dtype=np.float32))
