@@ -29,6 +29,26 @@ H, I, E, K = 7168, 2048, 256, 8
 SEED, WORKLOAD = 0, 3
 METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)"
 
+# HBM bytes per k_gate_up launch at bsz 1 from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
+# scaled by the same counter's reading for a 1 GiB device copy (profiles/
+# moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
+MEASURED_TRAFFIC = {
+    "sources_sha256": "82b0e1ee36ec5814717419518b5a496ff584d4c7ba4be433ee10be7b47bbf679",
+    "bytes_per_launch": 297734046,
+}
+KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h")
+
+
+def measured_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != MEASURED_TRAFFIC["sources_sha256"]:
+        return None  # the kernels changed since the counters were taken
+    return MEASURED_TRAFFIC["bytes_per_launch"]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -39,7 +59,21 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=4,
                    help="tokens (bsz 1 steps) the oracle times for the CPU baseline")
     p.add_argument("--bsz2", type=int, default=1, help="also time bsz 2 (0 to skip)")
+    p.add_argument("--calib-copy-mb", type=int, default=0,
+                   help="first run 3 plain device copies of this many MiB (a known-size "
+                        "reference for HBM byte counters under rocprofv3 --pmc)")
     return p.parse_args()
+
+
+def calib_copy(torch, mib):
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copies: 3 x %d bytes read + %d bytes written" % (n, n))
+    del src, dst
 
 
 def log(*a):
@@ -153,6 +187,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dm.lib()  # raises if the library is not built
+    if args.calib_copy_mb:
+        calib_copy(torch, args.calib_copy_mb)
 
     log("building layer: %d routed + 1 shared experts, fp9, %.2f GB" %
         (E, (E + 1) * 3 * H * I * 9 / 8 / 1e9))
@@ -203,7 +239,7 @@ def main():
             "frac": gu_gbps / HBM_PEAK_GBPS,
             "avg_launch_us": r1["gate_up_us"],
             "bytes_per_launch": r1["bytes_gate_up"],
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "cpu_baseline": None,
     }

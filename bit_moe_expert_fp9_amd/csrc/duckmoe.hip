@@ -36,6 +36,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "../../include/duckmoe.h"
 #include "fp9_device.h"
 
@@ -48,7 +51,21 @@ constexpr int kMaxSlots = kMaxIds + 1;
 constexpr int kMaxWords = DUCKMOE_MAX_ROUTED / 32;
 constexpr int kChunk = 1024;          // weights per wave-row step: 64 lanes x 16
 constexpr size_t kHdrBytes = 4096;    // workspace header (status, plan)
-constexpr int kXLdsBudget = 65536;    // bytes of LDS for the staged activations
+
+// Launch shape of the gate/up kernel (compile-time; defaults measured on MI355X).
+#ifndef DUCKMOE_GU_WAVES
+#define DUCKMOE_GU_WAVES 8     // waves per workgroup
+#endif
+#ifndef DUCKMOE_GU_PAIRS
+#define DUCKMOE_GU_PAIRS 1     // (gate, up) row pairs per wave task
+#endif
+#ifndef DUCKMOE_GU_PREFETCH
+#define DUCKMOE_GU_PREFETCH 1  // 1: next chunk's loads in flight while computing
+#endif
+#ifndef DUCKMOE_GU_WAVES_PER_CU
+#define DUCKMOE_GU_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+constexpr int kGuTokens = 4;   // tokens per gate/up pass (x of all of them sits in LDS)
 
 // Workspace header, written by block (0,0) of the gate/up launch.
 struct WsHeader {
@@ -78,11 +95,10 @@ struct PlanLds {
   int status;
   int expert[kMaxSlots];
   float w[kMaxSlots][kMaxT];
-  uint32_t bitmap[kMaxWords];
-  int prefix[kMaxWords];
 };
 
-__device__ void build_plan(PlanLds &P, const LayerArgs &a) {
+// bitmap/prefix: 2 * kMaxWords words of scratch LDS, free again on return.
+__device__ void build_plan(PlanLds &P, const LayerArgs &a, uint32_t *bitmap, int *prefix) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (a.ids == nullptr) {
     if (tid == 0) {
@@ -96,7 +112,7 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a) {
   }
   const int N = a.T * a.top_k;
   const int nwords = (a.n_routed + 31) >> 5;
-  for (int i = tid; i < nwords; i += nt) P.bitmap[i] = 0u;
+  for (int i = tid; i < nwords; i += nt) bitmap[i] = 0u;
   for (int i = tid; i < kMaxSlots * kMaxT; i += nt) (&P.w[0][0])[i] = 0.0f;
   if (tid == 0) P.status = 0;
   __syncthreads();
@@ -113,20 +129,20 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a) {
     if (!valid) {
       st |= DUCKMOE_STATUS_BAD_ID;
     } else {
-      atomicOr(&P.bitmap[id >> 5], 1u << (id & 31));
+      atomicOr(&bitmap[id >> 5], 1u << (id & 31));
       for (int j = base; j < tid; ++j)
         if (a.ids[j] == id) st |= DUCKMOE_STATUS_DUP_ID;
     }
     if (st) atomicOr(&P.status, st);
   }
   __syncthreads();
-  for (int i = tid; i < nwords; i += nt) P.prefix[i] = __popc(P.bitmap[i]);
+  for (int i = tid; i < nwords; i += nt) prefix[i] = __popc(bitmap[i]);
   __syncthreads();
   if (tid == 0) {
     int run = 0;
     for (int i = 0; i < nwords; ++i) {
-      const int c = P.prefix[i];
-      P.prefix[i] = run;
+      const int c = prefix[i];
+      prefix[i] = run;
       run += c;
     }
     P.n_slots = run + 1;
@@ -135,7 +151,7 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a) {
   __syncthreads();
   if (valid) {
     const int wd = id >> 5;
-    const int slot = P.prefix[wd] + __popc(P.bitmap[wd] & ((1u << (id & 31)) - 1u));
+    const int slot = prefix[wd] + __popc(bitmap[wd] & ((1u << (id & 31)) - 1u));
     P.expert[slot] = id;  // every lane holding this id writes the same value
     bool first = true;
     for (int j = base; j < tid; ++j)
@@ -154,232 +170,372 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ------------------------------------------------------------- gate / up ----
-// grid = (ceil(I / (P*WA)), max slots), block = WA waves.
-// Dynamic LDS: T * cpp * 1024 floats of activations (cpp chunks per phase).
-template <int T, int P, int WA>
-__global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const int cpp) {
-  __shared__ PlanLds plan;
-  extern __shared__ float4 xs4[];
-  build_plan(plan, a);
-  const int slot = blockIdx.y;
-  if (slot >= plan.n_slots) return;  // whole workgroup
-  if (blockIdx.x == 0 && slot == 0 && threadIdx.x == 0) {
-    a.hdr->status = plan.status;
-    a.hdr->n_slots = plan.n_slots;
-  }
-  const int H = a.H, I = a.I;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
-  const uint32_t mat = (uint32_t)I * (uint32_t)H;  // bytes of one body matrix
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
-  const int i0 = (blockIdx.x * WA + wave) * P;
-  const int nc = (H + kChunk - 1) / kChunk;
+// Persistent: grid = resident workgroups, WA waves each.  The tasks are
+// (expert slot, group of P intermediate rows); wave w of the grid takes tasks
+// w, w + NW, w + 2 NW, ... (NW = all waves).  A wave streams its tasks as one
+// sequence of (task, 1024-wide chunk of the hidden dim) units; with PF = 1 the
+// loads of the next unit are issued before the current one is computed, so a
+// wave keeps 2P rows of weights in flight while it decodes and multiplies.
+// The TG tokens t0 .. t0+TG-1 of the call are handled; their activations sit in
+// LDS for the whole kernel.  Dynamic LDS: max(TG * H, 2 * kMaxWords) floats.
+template <int P>
+struct GuTile {
+  uint4 d[2][P];
+  uint32_t s[2][P];
+};
 
-  // per-row lane offsets into the gate (g = 0) and up (g = 1) halves
-  uint32_t ob[2][P], os[2][P];
+struct GuUnit {              // where one (task, chunk) unit reads from
+  __amdgpu_buffer_rsrc_t rb, rs;
+  uint32_t row0;             // first intermediate row of the task
+  uint32_t kc;               // first weight of the chunk
+  int slot;
+  int task;
+  int c;                     // chunk index
+};
+
+template <int P>
+__device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, const PlanLds &plan, int task,
+                                          int c) {
+  const int NB = a.I / P;
+  const int slot = task / NB;
+  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+  const uint32_t mat = (uint32_t)a.I * (uint32_t)a.H;
+  GuUnit u;
+  u.rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
+  u.rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
+  u.row0 = (uint32_t)(task - slot * NB) * P;
+  u.kc = (uint32_t)c * kChunk;
+  u.slot = slot;
+  u.task = task;
+  u.c = c;
+  return u;
+}
+
+// The unit after u in a wave's sequence: next chunk, or chunk 0 of task + NW.
+template <int P>
+__device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const PlanLds &plan,
+                                          const GuUnit &u, int nc, int NW, int ntask) {
+  if (u.c + 1 < nc) {
+    GuUnit n = u;
+    n.c = u.c + 1;
+    n.kc = u.kc + kChunk;
+    return n;
+  }
+  if (u.task + NW < ntask) return gu_unit<P>(a, plan, u.task + NW, 0);
+  GuUnit n = u;
+  n.task = ntask;  // past the end
+  return n;
+}
+
+template <int P>
+__device__ __forceinline__ void gu_issue(GuTile<P> &b, const GuUnit &u, const LayerArgs &a,
+                                         int lane) {
+  const uint32_t H = a.H, I = a.I;
+  const bool kv = u.kc + lane * 16 < H;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int row = i0 + p;
-      const uint32_t r = (uint32_t)g * I + row;
-      ob[g][p] = row < I ? r * H + lane * 16 : kOutOfRange;
-      os[g][p] = row < I ? r * (H / 8) + lane * 2 : kOutOfRange;
+      const uint32_t r = g * I + u.row0 + p;
+      b.d[g][p] = buf_load16(u.rb, kv ? r * H + u.kc + lane * 16 : kOutOfRange);
+      b.s[g][p] = buf_load2(u.rs, kv ? r * (H / 8) + (u.kc + lane * 16) / 8 : kOutOfRange);
     }
+}
 
-  float acc[2][P][T][2];
+template <int TG, int P>
+__device__ __forceinline__ void gu_consume(const GuTile<P> &b, const float4 *xs4, int Hp4,
+                                           uint32_t kc, int lane, float (&acc)[2][P][TG][2]) {
+  float xv[TG][16];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const float4 *src = xs4 + t * Hp4 + kc / 4 + lane * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = src[j];
+      xv[t][4 * j + 0] = v.x;
+      xv[t][4 * j + 1] = v.y;
+      xv[t][4 * j + 2] = v.z;
+      xv[t][4 * j + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      h2_t h[8];
+      fp9_decode16(b.d[g][p], b.s[g][p], h);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) fma16(h, xv[t], acc[g][p][t][0], acc[g][p][t][1]);
+    }
+}
+
+template <int TG, int P>
+__device__ __forceinline__ void gu_finish(const LayerArgs &a, const PlanLds &plan, int slot,
+                                          uint32_t row0, int t0, int lane,
+                                          float (&acc)[2][P][TG][2]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float gsum = wave_sum(acc[0][p][t][0] + acc[0][p][t][1]);
+      const float vsum = wave_sum(acc[1][p][t][0] + acc[1][p][t][1]);
+      acc[0][p][t][0] = acc[0][p][t][1] = acc[1][p][t][0] = acc[1][p][t][1] = 0.0f;
+      if (lane == 0) {
+        const float wt = plan.w[slot][t0 + t];
+        const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gsum) * vsum);
+        a.hbuf[((size_t)slot * a.T + t0 + t) * a.I + row0 + p] = hv;
+      }
+    }
+}
+
+template <int TG, int P, int WA>
+__global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const int t0) {
+  __shared__ PlanLds plan;
+  extern __shared__ float4 xs4[];  // [TG][nc * 256]: rows padded with zeros to whole chunks
+  constexpr int NT = WA * 64;
+  constexpr int XR = 8;  // float4 of x per thread loaded before the plan
+  const int H = a.H, H4 = a.H / 4;
+  const int nc = (H + kChunk - 1) / kChunk;
+  const int Hp4 = nc * (kChunk / 4);
+  const int n4 = TG * Hp4;
+  const float4 *xg = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
+
+  // x loads first: their latency overlaps the plan's id loads
+  float4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int q = threadIdx.x + j * NT;
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    xr[j] = (q < n4 && k4 < H4) ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  build_plan(plan, a, reinterpret_cast<uint32_t *>(xs4),
+             reinterpret_cast<int *>(xs4) + kMaxWords);  // ends with a barrier
+  if (blockIdx.x == 0 && threadIdx.x == 0 && t0 == 0) {
+    a.hdr->status = plan.status;
+    a.hdr->n_slots = plan.n_slots;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NW = gridDim.x * WA;
+  const int gw = blockIdx.x * WA + wave;
+  const int ntask = plan.n_slots * (a.I / P);
+
+  GuTile<P> b0, b1;
+  GuUnit u0, u1;
+  u0.task = ntask;
+  if (gw < ntask) {
+    u0 = gu_unit<P>(a, plan, gw, 0);
+    gu_issue(b0, u0, a, lane);
+  }
+  // activations into LDS (the first XR float4 per thread are already loaded)
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int q = threadIdx.x + j * NT;
+    if (q < n4) xs4[q] = xr[j];
+  }
+  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) {
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    xs4[q] = k4 < H4 ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  float acc[2][P][TG][2];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int t = 0; t < T; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
+      for (int t = 0; t < TG; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
 
-  for (int c0 = 0; c0 < nc; c0 += cpp) {
-    const int cn = min(cpp, nc - c0);
-    const int per_t = cn * (kChunk / 4);  // float4 per token in this phase
-    __syncthreads();
-    for (int q = threadIdx.x; q < T * per_t; q += WA * 64) {
-      const int t = q / per_t, r = q - t * per_t;
-      const int k = c0 * kChunk + r * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < H) v = *reinterpret_cast<const float4 *>(a.x + (size_t)t * H + k);
-      xs4[q] = v;
-    }
-    __syncthreads();
-    for (int cc = 0; cc < cn; ++cc) {
-      const uint32_t kc = (uint32_t)(c0 + cc) * kChunk;
-      const bool kv = kc + lane * 16 < (uint32_t)H;
-      uint4 d[2][P];
-      uint32_t s[2][P];
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          d[g][p] = buf_load16(rb, kv ? ob[g][p] + kc : kOutOfRange);
-          s[g][p] = buf_load2(rs, kv ? os[g][p] + kc / 8 : kOutOfRange);
-        }
-      float xv[T][16];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 *src = xs4 + t * per_t + cc * (kChunk / 4) + lane * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 v = src[j];
-          xv[t][4 * j + 0] = v.x;
-          xv[t][4 * j + 1] = v.y;
-          xv[t][4 * j + 2] = v.z;
-          xv[t][4 * j + 3] = v.w;
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          h2_t h[8];
-          fp9_decode16(d[g][p], s[g][p], h);
-#pragma unroll
-          for (int t = 0; t < T; ++t) fma16(h, xv[t], acc[g][p][t][0], acc[g][p][t][1]);
-        }
-    }
-  }
+  // Two units per trip so that the register buffers keep static names.
+  while (u0.task < ntask) {
+    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+    if (DUCKMOE_GU_PREFETCH && u1.task < ntask) gu_issue(b1, u1, a, lane);
+    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc);
+    if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
+    if (u1.task >= ntask) break;
+    if (!DUCKMOE_GU_PREFETCH) gu_issue(b1, u1, a, lane);
 
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int row = i0 + p;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float gsum = wave_sum(acc[0][p][t][0] + acc[0][p][t][1]);
-      const float vsum = wave_sum(acc[1][p][t][0] + acc[1][p][t][1]);
-      if (lane == 0 && row < I) {
-        const float wt = plan.w[slot][t];
-        const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gsum) * vsum);
-        a.hbuf[((size_t)slot * T + t) * I + row] = hv;
-      }
-    }
+    u0 = gu_next<P>(a, plan, u1, nc, NW, ntask);
+    if (DUCKMOE_GU_PREFETCH && u0.task < ntask) gu_issue(b0, u0, a, lane);
+    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc);
+    if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
+    if (!DUCKMOE_GU_PREFETCH && u0.task < ntask) gu_issue(b0, u0, a, lane);
   }
 }
 
 // ------------------------------------------------------------------ down ----
-// grid = ceil(H / R), block = WB waves.  Wave w handles chunk c = w % nc of the
-// intermediate dimension for slots w / nc, w / nc + WB / nc, ...
-// Dynamic LDS: WB * R * T * 16 floats (lane-group partial sums).
+// Persistent: grid = resident workgroups of WB waves; workgroup g takes the
+// blocks of R output rows g, g + G, ...  Within a block the waves split the
+// (expert slot, 1024-wide chunk of the intermediate dim) items: wave w works
+// on chunk c = w % nc for slots w / nc, w / nc + WB / nc, ...  A wave streams
+// its items of all its blocks as one sequence, loading the next item while it
+// computes the current one (also across blocks).  At the end of a block each
+// wave reduces its lanes in groups as wide as a shard slice, the groups' sums
+// meet in LDS, and the waves' sums are added in a fixed order: each output
+// element is written once, no atomics, bit-reproducible.
+// Dynamic LDS: max(WB * R * T * 16, 2 * kMaxWords) floats.
 template <int G>
 __device__ __forceinline__ void store_groups(float v, float *dst, int lane) {
   v = group_sum<G>(v);
   if ((lane & (G - 1)) == G - 1) dst[lane / G] = v;
 }
 
+template <int T, int R>
+struct DnTile {
+  uint4 d[R];
+  uint32_t s[R];
+  float4 h[T][4];  // the item's activations h'[slot][t][k .. k+16)
+};
+
+template <int T, int R>
+__device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, const PlanLds &plan,
+                                         __amdgpu_buffer_rsrc_t rh, int slot, int row0,
+                                         uint32_t k, bool kv) {
+  const uint32_t H = a.H, I = a.I;
+  const uint32_t mat = H * I;
+  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = row0 + r;
+    const bool ok = kv && row < H;
+    b.d[r] = buf_load16(rb, ok ? row * I + k : kOutOfRange);
+    b.s[r] = buf_load2(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint32_t off = kv ? ((uint32_t)(slot * a.T + t) * I + k) * 4u : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.h[t][j] = buf_loadf4(rh, off + 16 * j);
+  }
+}
+
+template <int T, int R>
+__device__ __forceinline__ void dn_consume(const DnTile<T, R> &b, float (&acc)[R][T][2]) {
+  float hv[T][16];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = b.h[t][j];
+      hv[t][4 * j + 0] = v.x;
+      hv[t][4 * j + 1] = v.y;
+      hv[t][4 * j + 2] = v.z;
+      hv[t][4 * j + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    h2_t h[8];
+    fp9_decode16(b.d[r], b.s[r], h);
+#pragma unroll
+    for (int t = 0; t < T; ++t) fma16(h, hv[t], acc[r][t][0], acc[r][t][1]);
+  }
+}
+
+// The n_it items (slots s0, s0 + per_c, ...) of one block for one wave.  The
+// first item is already in flight in b0; items alternate between b0 and b1,
+// the next one always issued before the current one is computed.
+template <int T, int R>
+__device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, const LayerArgs &a,
+                                         const PlanLds &plan, __amdgpu_buffer_rsrc_t rh,
+                                         int blk, int s0, int per_c, int n_it, uint32_t k,
+                                         bool kv, float (&acc)[R][T][2]) {
+  for (int i = 0; i < n_it; i += 2) {
+    const int slot = s0 + i * per_c;
+    if (i + 1 < n_it) dn_issue<T, R>(b1, a, plan, rh, slot + per_c, blk * R, k, kv);
+    dn_consume<T, R>(b0, acc);
+    if (i + 1 >= n_it) break;
+    if (i + 2 < n_it) dn_issue<T, R>(b0, a, plan, rh, slot + 2 * per_c, blk * R, k, kv);
+    dn_consume<T, R>(b1, acc);
+  }
+}
+
 template <int T, int R, int WB>
 __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G) {
   __shared__ PlanLds plan;
   extern __shared__ float red[];
-  build_plan(plan, a);
+  build_plan(plan, a, reinterpret_cast<uint32_t *>(red), reinterpret_cast<int *>(red) + kMaxWords);
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = blockIdx.x * R;
   const int nc = (I + kChunk - 1) / kChunk;
   const int per_c = WB / nc;  // waves per chunk
   const int S = plan.n_slots;
-  const uint32_t mat = (uint32_t)H * (uint32_t)I;
-  const uint32_t hbytes = (uint32_t)(S * T * I) * 4u;
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, hbytes);
-
-  float acc[R][T][2];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[r][t][0] = acc[r][t][1] = 0.0f;
-
-  if (wave < nc * per_c) {
-    const int c = wave % nc;
-    const uint32_t k = (uint32_t)c * kChunk + lane * 16;
-    const bool kv = k < (uint32_t)I;
-    uint32_t ob[R], os[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = row0 + r;
-      ob[r] = (kv && row < H) ? (uint32_t)row * I + k : kOutOfRange;
-      os[r] = (kv && row < H) ? (uint32_t)row * (I / 8) + k / 8 : kOutOfRange;
-    }
-    for (int slot = wave / nc; slot < S; slot += per_c) {
-      const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
-      uint4 d[R];
-      uint32_t s[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        d[r] = buf_load16(rb, ob[r]);
-        s[r] = buf_load2(rs, os[r]);
-      }
-      float hv[T][16];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint32_t off = kv ? ((uint32_t)(slot * T + t) * I + k) * 4u : kOutOfRange;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 v = buf_loadf4(rh, off + 16 * j);
-          hv[t][4 * j + 0] = v.x;
-          hv[t][4 * j + 1] = v.y;
-          hv[t][4 * j + 2] = v.z;
-          hv[t][4 * j + 3] = v.w;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        h2_t h[8];
-        fp9_decode16(d[r], s[r], h);
-#pragma unroll
-        for (int t = 0; t < T; ++t) fma16(h, hv[t], acc[r][t][0], acc[r][t][1]);
-      }
-    }
-  }
-
-  // lane groups of G lanes -> 64/G partial sums per (wave, row, token)
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float *dst = red + ((wave * R + r) * T + t) * 16;
-      const float v = acc[r][t][0] + acc[r][t][1];
-      switch (G) {
-        case 4: store_groups<4>(v, dst, lane); break;
-        case 8: store_groups<8>(v, dst, lane); break;
-        case 16: store_groups<16>(v, dst, lane); break;
-        case 32: store_groups<32>(v, dst, lane); break;
-        default: store_groups<64>(v, dst, lane); break;
-      }
-    }
-  __syncthreads();
-
-  // combine: output (shard, t, row).  Slice width = I / n_shards.
+  const int nblk = (H + R - 1) / R;
+  const int c = wave % nc;
+  const uint32_t k = (uint32_t)c * kChunk + lane * 16;
+  const bool kv = k < (uint32_t)I;
+  const int s0 = wave / nc;  // first slot of this wave in every block
+  // items per block for this wave (0 for waves beyond nc * per_c)
+  const int n_it = (wave < nc * per_c && s0 < S) ? (S - s0 + per_c - 1) / per_c : 0;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, (uint32_t)(S * a.T * I) * 4u);
   const int ns = a.n_shards;
   const int width = I / ns;
-  for (int q = threadIdx.x; q < ns * T * R; q += WB * 64) {
-    const int shard = q / (T * R);
-    const int rem = q - shard * (T * R);
-    const int t = rem / R, r = rem - t * R;
-    const int row = row0 + r;
-    if (row >= H) continue;
-    int c_lo, c_hi, grp;
-    if (ns == 1) {
-      c_lo = 0; c_hi = nc; grp = 0;
-    } else if (width >= kChunk) {
-      c_lo = shard * (width / kChunk); c_hi = c_lo + width / kChunk; grp = 0;
-    } else {
-      c_lo = (shard * width) / kChunk; c_hi = c_lo + 1;
-      grp = ((shard * width) % kChunk) / (G * 16);
+
+  DnTile<T, R> b0, b1;
+  if (n_it > 0 && (int)blockIdx.x < nblk)
+    dn_issue<T, R>(b0, a, plan, rh, s0, blockIdx.x * R, k, kv);
+
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    float acc[R][T][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t][0] = acc[r][t][1] = 0.0f;
+
+    if (n_it > 0) {
+      dn_block<T, R>(b0, b1, a, plan, rh, blk, s0, per_c, n_it, k, kv, acc);
+      // the next block's first item loads while this block is reduced
+      if (blk + (int)gridDim.x < nblk)
+        dn_issue<T, R>(b0, a, plan, rh, s0, (blk + gridDim.x) * R, k, kv);
     }
-    float sum = 0.0f;
-    for (int w = 0; w < nc * per_c; ++w) {
-      const int c = w % nc;
-      if (c >= c_lo && c < c_hi) sum += red[((w * R + r) * T + t) * 16 + grp];
+
+    // lane groups of G lanes -> 64/G partial sums per (wave, row, token)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float *dst = red + ((wave * R + r) * T + t) * 16;
+        const float v = acc[r][t][0] + acc[r][t][1];
+        switch (G) {
+          case 4: store_groups<4>(v, dst, lane); break;
+          case 8: store_groups<8>(v, dst, lane); break;
+          case 16: store_groups<16>(v, dst, lane); break;
+          case 32: store_groups<32>(v, dst, lane); break;
+          default: store_groups<64>(v, dst, lane); break;
+        }
+      }
+    __syncthreads();
+
+    // combine: output (shard, t, row)
+    const int row0 = blk * R;
+    for (int q = threadIdx.x; q < ns * T * R; q += WB * 64) {
+      const int shard = q / (T * R);
+      const int rem = q - shard * (T * R);
+      const int t = rem / R, r = rem - t * R;
+      const int row = row0 + r;
+      if (row >= H) continue;
+      int c_lo, c_hi, grp;
+      if (ns == 1) {
+        c_lo = 0; c_hi = nc; grp = 0;
+      } else if (width >= kChunk) {
+        c_lo = shard * (width / kChunk); c_hi = c_lo + width / kChunk; grp = 0;
+      } else {
+        c_lo = (shard * width) / kChunk; c_hi = c_lo + 1;
+        grp = ((shard * width) % kChunk) / (G * 16);
+      }
+      float sum = 0.0f;
+      for (int w = 0; w < nc * per_c; ++w) {
+        const int cw = w % nc;
+        if (cw >= c_lo && cw < c_hi) sum += red[((w * R + r) * T + t) * 16 + grp];
+      }
+      a.out[((size_t)shard * T + t) * H + row] = sum;
     }
-    a.out[((size_t)shard * T + t) * H + row] = sum;
+    __syncthreads();  // red is rewritten by the next block
   }
 }
 
@@ -445,13 +601,24 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ body,
 
 __global__ __launch_bounds__(64) void k_plan(const LayerArgs a, int32_t *uniq, int32_t *n_slots) {
   __shared__ PlanLds plan;
-  build_plan(plan, a);
+  __shared__ uint32_t scratch[2 * kMaxWords];
+  build_plan(plan, a, scratch, reinterpret_cast<int *>(scratch) + kMaxWords);
   for (int s = threadIdx.x; s < plan.n_slots; s += blockDim.x) uniq[s] = plan.expert[s];
   if (threadIdx.x == 0) *n_slots = plan.n_slots;
 }
 
 // ------------------------------------------------------------ host side ----
 bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+constexpr size_t kGuXLds = 131072;  // LDS bytes for the activations of one gate/up pass
+
+// tokens the gate/up kernel takes per pass for a given hidden size (0: too wide)
+int gu_tokens_per_pass(int H) {
+  const size_t hp = (size_t)((H + kChunk - 1) / kChunk) * kChunk;
+  return (int)std::min<size_t>(kGuTokens, kGuXLds / (hp * sizeof(float)));
+}
+
+
 
 int check_layer(const duckmoe_layer *L) {
   if (!L || !L->gu_body || !L->gu_sign || !L->dn_body || !L->dn_sign) return DUCKMOE_EINVAL;
@@ -460,6 +627,7 @@ int check_layer(const duckmoe_layer *L) {
     return DUCKMOE_ESHAPE;
   // one buffer descriptor spans an expert's gate+up bodies: 2*H*I < 2^31
   if (2ll * L->hidden * L->inter > 0x7fffffffll) return DUCKMOE_ESHAPE;
+  if (gu_tokens_per_pass(L->hidden) < 1) return DUCKMOE_ESHAPE;
   if (!aligned(L->gu_body, 16) || !aligned(L->dn_body, 16) || !aligned(L->gu_sign, 2) ||
       !aligned(L->dn_sign, 2))
     return DUCKMOE_EINVAL;
@@ -489,47 +657,92 @@ size_t ws_need(const duckmoe_layer *L, int T, bool single) {
   return kHdrBytes + hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
 }
 
-constexpr int kWA = 4;   // waves per gate/up workgroup
-constexpr int kWB = 6;   // waves per down workgroup
+// Launch shape of the down kernel (compile-time; defaults measured on MI355X).
+#ifndef DUCKMOE_DN_WAVES
+#define DUCKMOE_DN_WAVES 2          // waves per workgroup
+#endif
+#ifndef DUCKMOE_DN_ROWS
+#define DUCKMOE_DN_ROWS 4           // output rows per block at T = 1 (see down_rows)
+#endif
+#ifndef DUCKMOE_DN_WAVES_PER_CU
+#define DUCKMOE_DN_WAVES_PER_CU 8   // target resident waves per CU (capped by occupancy)
+#endif
+constexpr int kWB = DUCKMOE_DN_WAVES;
 
+// rows per down block: more rows share each h' load, fewer keep registers in check
 template <int T>
-constexpr int pairs_per_wave() { return T <= 4 ? 4 : 2; }
-template <int T>
-constexpr int down_rows() { return T <= 2 ? 16 : (T <= 4 ? 8 : 4); }
+constexpr int down_rows() {
+  return T == 1 ? DUCKMOE_DN_ROWS : (T == 2 ? 2 * DUCKMOE_DN_ROWS : (T <= 4 ? DUCKMOE_DN_ROWS : 2));
+}
 
-template <int T>
-hipError_t launch_gate_up_t(const LayerArgs &a, int slots, hipStream_t st) {
-  constexpr int P = pairs_per_wave<T>();
-  const int nc = (a.H + kChunk - 1) / kChunk;
-  int cpp = kXLdsBudget / (T * kChunk * (int)sizeof(float));
-  cpp = max(1, min(cpp, nc));
-  const size_t lds = (size_t)T * cpp * kChunk * sizeof(float);
-  const dim3 grid((a.I + P * kWA - 1) / (P * kWA), slots);
-  hipLaunchKernelGGL((k_gate_up<T, P, kWA>), grid, dim3(kWA * 64), lds, st, a, cpp);
+// Compute units of the current device, cached per device id.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+template <int TG>
+hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
+  constexpr int P = DUCKMOE_GU_PAIRS, WA = DUCKMOE_GU_WAVES;
+  const auto kern = k_gate_up<TG, P, WA>;
+  const size_t hp = (size_t)((a.H + kChunk - 1) / kChunk) * kChunk;
+  const size_t lds = std::max((size_t)TG * hp * sizeof(float), (size_t)2 * kMaxWords * 4);
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  int per_cu = 0;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WA * 64, lds);
+  if (err != hipSuccess) return err;
+  const int cus = device_cus();
+  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  per_cu = std::max(1, std::min(per_cu, DUCKMOE_GU_WAVES_PER_CU / WA));
+  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(WA * 64), lds, st, a, t0);
   return hipGetLastError();
 }
 
 template <int T>
 hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
   constexpr int R = down_rows<T>();
-  const size_t lds = (size_t)kWB * R * T * 16 * sizeof(float);
-  const dim3 grid((a.H + R - 1) / R);
-  hipLaunchKernelGGL((k_down<T, R, kWB>), grid, dim3(kWB * 64), lds, st, a,
+  const auto kern = k_down<T, R, kWB>;
+  const size_t lds = std::max((size_t)kWB * R * T * 16 * sizeof(float),
+                              (size_t)2 * kMaxWords * 4);
+  int per_cu = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWB * 64, lds);
+  if (err != hipSuccess) return err;
+  const int cus = device_cus();
+  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  per_cu = std::max(1, std::min(per_cu, DUCKMOE_DN_WAVES_PER_CU / kWB));
+  const int nblk = (a.H + R - 1) / R;
+  const int grid = std::min(nblk, cus * per_cu);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWB * 64), lds, st, a,
                      group_width(a.I, a.n_shards));
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up(const LayerArgs &a, int slots, hipStream_t st) {
-  switch (a.T) {
-    case 1: return launch_gate_up_t<1>(a, slots, st);
-    case 2: return launch_gate_up_t<2>(a, slots, st);
-    case 3: return launch_gate_up_t<3>(a, slots, st);
-    case 4: return launch_gate_up_t<4>(a, slots, st);
-    case 5: return launch_gate_up_t<5>(a, slots, st);
-    case 6: return launch_gate_up_t<6>(a, slots, st);
-    case 7: return launch_gate_up_t<7>(a, slots, st);
-    default: return launch_gate_up_t<8>(a, slots, st);
+hipError_t launch_gate_up(const LayerArgs &a, hipStream_t st) {
+  const int tpp = gu_tokens_per_pass(a.H);
+  for (int t0 = 0; t0 < a.T; t0 += tpp) {
+    hipError_t err;
+    switch (std::min(tpp, a.T - t0)) {
+      case 1: err = launch_gate_up_t<1>(a, t0, st); break;
+      case 2: err = launch_gate_up_t<2>(a, t0, st); break;
+      case 3: err = launch_gate_up_t<3>(a, t0, st); break;
+      default: err = launch_gate_up_t<4>(a, t0, st); break;
+    }
+    if (err != hipSuccess) return err;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
@@ -584,8 +797,7 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   a.hbuf = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes);
 
   if (stages & kGateUp) {
-    if (launch_gate_up(a, (int)hbuf_slots(L, T, single), stream) != hipSuccess)
-      return DUCKMOE_EHIP;
+    if (launch_gate_up(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   }
   if (stages & kDown) {
     if (launch_down(a, stream) != hipSuccess) return DUCKMOE_EHIP;
