@@ -8,8 +8,9 @@ decode batch 1 (and 2, reported alongside).  A step is one full layer call
 step streams the selected experts from HBM rather than from cache.
 
 Prints one JSON line.  `value` is layer tokens/s at bsz 1 with inputs already
-in HBM.  The roofline object is for the dominant kernel (gate/up: two thirds
-of the bytes), timed with HIP events on the stream it runs on.  The CPU
+in HBM.  The roofline object is for the dominant kernel, k_gate_up (two thirds
+of the bytes): a second timed loop launches the two stages of the layer
+separately with HIP events around each, on the stream they run on.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload.
 """
 
@@ -29,12 +30,12 @@ H, I, E, K = 7168, 2048, 256, 8
 SEED, WORKLOAD = 0, 3
 METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)"
 
-# HBM bytes per k_gate_up launch at bsz 1 from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
-# scaled by the same counter's reading for a 1 GiB device copy (profiles/
+# HBM bytes per k_gate_up launch at bsz 1 from rocprofv3 FETCH_SIZE + WRITE_SIZE,
+# each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "82b0e1ee36ec5814717419518b5a496ff584d4c7ba4be433ee10be7b47bbf679",
-    "bytes_per_launch": 297734046,
+    "sources_sha256": "94537c48b3f09de32ad80e610155bb319e79890da04ca9fd8257a9b6c2cbec4d",
+    "bytes_per_launch": 297732859,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h")
 
@@ -104,40 +105,90 @@ def time_layer(torch, dm, layer, T, steps, warmup, draws):
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
     torch.cuda.synchronize()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         s = warmup + k
-        ev[2 * k].record(stream)
-        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
-        ev[2 * k + 1].record(stream)
-        dm.moe_down(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
-    ev[2 * steps].record(stream)
+        ev[k].record(stream)
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+    ev[steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = ev[0].elapsed_time(ev[2 * steps])
-    t_gu = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)])
-    t_dn = np.array([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(steps)])
+    total_ms = ev[0].elapsed_time(ev[steps])
+    t_call = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    st = dm.status(ws)
+    if st & dm.duckmoe.STATUS_TIMEOUT:
+        raise RuntimeError("layer call reported an in-kernel timeout")
     u = np.array(uniq[warmup:], dtype=np.float64)
     eb = layer.expert_bytes()
-    bytes_gu = (u + 1) * (2 * eb / 3) + T * H * 4
-    bytes_dn = (u + 1) * (eb / 3) + T * H * 4
+    bytes_call = (u + 1) * eb + 2 * T * H * 4   # selected experts' fp9 planes + x + out
     return {
         "T": T,
         "total_ms": total_ms,
         "wall_s": wall,
         "ms_per_step": total_ms / steps,
         "tokens_per_s": T * steps / (total_ms / 1e3),
-        "gate_up_us": float(t_gu.mean() * 1e3),
-        "down_us": float(t_dn.mean() * 1e3),
-        "bytes_gate_up": float(bytes_gu.mean()),
-        "bytes_down": float(bytes_dn.mean()),
-        "bytes_step": float((bytes_gu + bytes_dn).mean()),
+        "call_us": float(t_call.mean() * 1e3),
+        "bytes_step": float(bytes_call.mean()),
         "mean_experts": float((u + 1).mean()),
-        "p10_us": float(np.percentile(t_gu + t_dn, 10) * 1e3),
-        "p50_us": float(np.percentile(t_gu + t_dn, 50) * 1e3),
-        "p90_us": float(np.percentile(t_gu + t_dn, 90) * 1e3),
+        "p10_us": float(np.percentile(t_call, 10) * 1e3),
+        "p50_us": float(np.percentile(t_call, 50) * 1e3),
+        "p90_us": float(np.percentile(t_call, 90) * 1e3),
+    }
+
+
+def time_stages(torch, dm, layer, T, steps, warmup, draws):
+    """Times the gate/up and down stages launched one by one (HIP events around each)."""
+    from bit_moe_expert_fp9_amd import synth
+    n = steps + warmup
+    xs, ids, ws_, uniq = [], [], [], []
+    for s in range(n):
+        d = s % draws
+        x = synth.activations(SEED, WORKLOAD, 0, 30_000 + d, T, H)
+        i, w = synth.routing(SEED, WORKLOAD, 0, 30_000 + d, T, E, K)
+        xs.append(x)
+        ids.append(i)
+        ws_.append(w)
+        uniq.append(len(np.unique(i)))
+    X = torch.from_numpy(np.stack(xs)).cuda()
+    IDS = torch.from_numpy(np.stack(ids)).cuda()
+    W = torch.from_numpy(np.stack(ws_)).cuda()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T)
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+        dm.moe_down(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for k in range(steps):
+        s = warmup + k
+        ev[3 * k].record(stream)
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+        ev[3 * k + 1].record(stream)
+        dm.moe_down(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+        ev[3 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    if dm.status(ws) & dm.duckmoe.STATUS_TIMEOUT:
+        raise RuntimeError("layer call reported an in-kernel timeout")
+    gu = np.array([ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(steps)]) * 1e3
+    dn = np.array([ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(steps)]) * 1e3
+    slots = np.array(uniq[warmup:], dtype=np.float64) + 1
+    eb = layer.expert_bytes()
+    # algorithmic bytes: gate/up reads 2/3 of each selected expert's planes and x and
+    # writes one h' row per slot and token; down reads the last 1/3 and the h' rows
+    # and writes out
+    gu_bytes = slots * (eb * 2 // 3) + T * H * 4 + slots * T * I * 4
+    dn_bytes = slots * (eb // 3) + slots * T * I * 4 + T * H * 4
+    return {
+        "T": T,
+        "gate_up_us": float(gu.mean()),
+        "down_us": float(dn.mean()),
+        "gate_up_bytes": float(gu_bytes.mean()),
+        "down_bytes": float(dn_bytes.mean()),
+        "gate_up_gbps": float(gu_bytes.mean() / (gu.mean() * 1e-6) / 1e9),
+        "down_gbps": float(dn_bytes.mean() / (dn.mean() * 1e-6) / 1e9),
     }
 
 
@@ -204,8 +255,10 @@ def main():
         r2 = time_layer(torch, dm, layer, 2, args.steps, args.warmup, draws)
         log("bsz2:", json.dumps(r2))
 
+    st1 = time_stages(torch, dm, layer, 1, args.steps, args.warmup, draws)
+    log("bsz1 stages:", json.dumps(st1))
+
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
-    gu_gbps = r1["bytes_gate_up"] / (r1["gate_up_us"] * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": r1["tokens_per_s"],
@@ -229,16 +282,18 @@ def main():
             "bsz2_tokens_per_s": r2["tokens_per_s"] if r2 else None,
             "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
             "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
+            "stages_us": {"k_gate_up": st1["gate_up_us"], "k_down": st1["down_us"]},
+            "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gate_up (gate/up GEMVs + SwiGLU)",
-            "achieved": gu_gbps,
+            "kernel": "k_gate_up (gate and up GEMVs + SwiGLU for every selected expert)",
+            "achieved": st1["gate_up_gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": gu_gbps / HBM_PEAK_GBPS,
-            "avg_launch_us": r1["gate_up_us"],
-            "bytes_per_launch": r1["bytes_gate_up"],
+            "frac": st1["gate_up_gbps"] / HBM_PEAK_GBPS,
+            "avg_launch_us": st1["gate_up_us"],
+            "bytes_per_launch": st1["gate_up_bytes"],
             "traffic": measured_traffic(),
         },
         "cpu_baseline": None,

@@ -50,7 +50,7 @@ constexpr int kMaxIds = DUCKMOE_MAX_IDS;
 constexpr int kMaxSlots = kMaxIds + 1;
 constexpr int kMaxWords = DUCKMOE_MAX_ROUTED / 32;
 constexpr int kChunk = 1024;          // weights per wave-row step: 64 lanes x 16
-constexpr size_t kHdrBytes = 4096;    // workspace header (status, plan)
+constexpr size_t kHdrBytes = 16384;   // workspace header (status, plan size, fused-path counters)
 
 // Launch shape of the gate/up kernel (compile-time; defaults measured on MI355X).
 #ifndef DUCKMOE_GU_WAVES
@@ -67,11 +67,14 @@ constexpr size_t kHdrBytes = 4096;    // workspace header (status, plan)
 #endif
 constexpr int kGuTokens = 4;   // tokens per gate/up pass (x of all of them sits in LDS)
 
-// Workspace header, written by block (0,0) of the gate/up launch.
+// Workspace header, written by block 0 of the gate/up launch: the status word
+// and, at kPlanOff, the plan (slot count and expert of each slot) that the down
+// launch reads instead of rebuilding it.
 struct WsHeader {
   int32_t status;
   int32_t n_slots;
 };
+constexpr size_t kPlanOff = 4096;
 
 struct LayerArgs {
   int H, I, n_routed, top_k, T, n_shards;
@@ -95,10 +98,30 @@ struct PlanLds {
   int status;
   int expert[kMaxSlots];
   float w[kMaxSlots][kMaxT];
+  int id[kMaxIds];      // the routed ids and weights, staged for the loops below
+  float wi[kMaxIds];
 };
 
+// Thread tid < T * top_k loads its id and weight before anything else, so that
+// the plan's first global round trip is not queued behind other loads.
+struct PlanIn {
+  int id;
+  float w;
+};
+
+__device__ __forceinline__ PlanIn plan_load(const LayerArgs &a) {
+  PlanIn in{-1, 0.0f};
+  const int tid = threadIdx.x;
+  if (a.ids != nullptr && tid < a.T * a.top_k) {
+    in.id = a.ids[tid];
+    if (a.w != nullptr) in.w = a.w[tid];
+  }
+  return in;
+}
+
 // bitmap/prefix: 2 * kMaxWords words of scratch LDS, free again on return.
-__device__ void build_plan(PlanLds &P, const LayerArgs &a, uint32_t *bitmap, int *prefix) {
+__device__ void build_plan(PlanLds &P, const LayerArgs &a, const PlanIn in, uint32_t *bitmap,
+                           int *prefix) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (a.ids == nullptr) {
     if (tid == 0) {
@@ -115,23 +138,24 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a, uint32_t *bitmap, int
   for (int i = tid; i < nwords; i += nt) bitmap[i] = 0u;
   for (int i = tid; i < kMaxSlots * kMaxT; i += nt) (&P.w[0][0])[i] = 0.0f;
   if (tid == 0) P.status = 0;
+  if (tid < N) {
+    P.id[tid] = in.id;
+    P.wi[tid] = in.w;
+  }
   __syncthreads();
 
-  int id = -1;
-  bool valid = false;
-  int tok = 0, base = 0;
+  const int id = in.id;
+  const bool valid = tid < N && id >= 0 && id < a.n_routed;
+  const int tok = tid < N ? tid / a.top_k : 0;
+  const int base = tok * a.top_k;
   if (tid < N) {
-    id = a.ids[tid];
-    valid = id >= 0 && id < a.n_routed;
-    tok = tid / a.top_k;
-    base = tok * a.top_k;
     int st = 0;
     if (!valid) {
       st |= DUCKMOE_STATUS_BAD_ID;
     } else {
       atomicOr(&bitmap[id >> 5], 1u << (id & 31));
       for (int j = base; j < tid; ++j)
-        if (a.ids[j] == id) st |= DUCKMOE_STATUS_DUP_ID;
+        if (P.id[j] == id) st |= DUCKMOE_STATUS_DUP_ID;
     }
     if (st) atomicOr(&P.status, st);
   }
@@ -155,12 +179,12 @@ __device__ void build_plan(PlanLds &P, const LayerArgs &a, uint32_t *bitmap, int
     P.expert[slot] = id;  // every lane holding this id writes the same value
     bool first = true;
     for (int j = base; j < tid; ++j)
-      if (a.ids[j] == id) first = false;
-    if (first && a.w != nullptr) {
-      float s = 0.0f;
+      if (P.id[j] == id) first = false;
+    if (first) {
+      float sum = 0.0f;
       for (int j = base; j < base + a.top_k; ++j)
-        if (a.ids[j] == id) s += a.w[j];
-      P.w[slot][tok] = s;
+        if (P.id[j] == id) sum += P.wi[j];
+      P.w[slot][tok] = sum;
     }
   }
   if (tid < a.T) P.w[P.n_slots - 1][tid] = 1.0f;
@@ -300,7 +324,8 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
   const int n4 = TG * Hp4;
   const float4 *xg = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
 
-  // x loads first: their latency overlaps the plan's id loads
+  // ids first, then x: the x loads' latency overlaps the plan
+  const PlanIn pin = plan_load(a);
   float4 xr[XR];
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
@@ -308,11 +333,16 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
     const int t = q / Hp4, k4 = q - t * Hp4;
     xr[j] = (q < n4 && k4 < H4) ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  build_plan(plan, a, reinterpret_cast<uint32_t *>(xs4),
+  build_plan(plan, a, pin, reinterpret_cast<uint32_t *>(xs4),
              reinterpret_cast<int *>(xs4) + kMaxWords);  // ends with a barrier
-  if (blockIdx.x == 0 && threadIdx.x == 0 && t0 == 0) {
-    a.hdr->status = plan.status;
-    a.hdr->n_slots = plan.n_slots;
+  if (blockIdx.x == 0 && t0 == 0) {
+    int32_t *wsplan = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(a.hdr) + kPlanOff);
+    if (threadIdx.x == 0) {
+      a.hdr->status = plan.status;
+      a.hdr->n_slots = plan.n_slots;
+      wsplan[0] = plan.n_slots;
+    }
+    for (int i = threadIdx.x; i < plan.n_slots; i += NT) wsplan[1 + i] = plan.expert[i];
   }
 
   const int lane = threadIdx.x & 63;
@@ -390,12 +420,12 @@ struct DnTile {
 };
 
 template <int T, int R>
-__device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, const PlanLds &plan,
+__device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, const int32_t *plan,
                                          __amdgpu_buffer_rsrc_t rh, int slot, int row0,
                                          uint32_t k, bool kv) {
   const uint32_t H = a.H, I = a.I;
   const uint32_t mat = H * I;
-  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+  const int e = __builtin_amdgcn_readfirstlane(plan[1 + slot]);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
 #pragma unroll
@@ -441,7 +471,7 @@ __device__ __forceinline__ void dn_consume(const DnTile<T, R> &b, float (&acc)[R
 // the next one always issued before the current one is computed.
 template <int T, int R>
 __device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, const LayerArgs &a,
-                                         const PlanLds &plan, __amdgpu_buffer_rsrc_t rh,
+                                         const int32_t *plan, __amdgpu_buffer_rsrc_t rh,
                                          int blk, int s0, int per_c, int n_it, uint32_t k,
                                          bool kv, float (&acc)[R][T][2]) {
   for (int i = 0; i < n_it; i += 2) {
@@ -456,15 +486,16 @@ __device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, con
 
 template <int T, int R, int WB>
 __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G) {
-  __shared__ PlanLds plan;
   extern __shared__ float red[];
-  build_plan(plan, a, reinterpret_cast<uint32_t *>(red), reinterpret_cast<int *>(red) + kMaxWords);
+  // the plan the gate/up launch left in the workspace (uniform scalar loads)
+  const int32_t *plan = reinterpret_cast<const int32_t *>(
+      reinterpret_cast<const uint8_t *>(a.hdr) + kPlanOff);
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nc = (I + kChunk - 1) / kChunk;
   const int per_c = WB / nc;  // waves per chunk
-  const int S = plan.n_slots;
+  const int S = __builtin_amdgcn_readfirstlane(plan[0]);
   const int nblk = (H + R - 1) / R;
   const int c = wave % nc;
   const uint32_t k = (uint32_t)c * kChunk + lane * 16;
@@ -539,6 +570,484 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
   }
 }
 
+// ----------------------------------------------------------------- fused ----
+// One launch for the whole layer (T <= 2).  The intermediate dimension is cut
+// into n_xcd slices of Ix = I / n_xcd rows, one per XCD of the chip (logical
+// XCD of workgroup b: b % n_xcd, which is where the hardware places it); each
+// XCD is a tensor-parallel shard in the pages' sense:
+//   A. its workgroups stream the gate/up rows of their slice for every plan
+//      slot (balanced contiguous ranges of (row pair, 1024-chunk) units per
+//      wave; a pair split between two waves is completed through LDS) and
+//      write h' with write-through stores;
+//   B. once every workgroup of the XCD has finished A (one counter per XCD),
+//      each workgroup stages the XCD's h' slice in LDS and streams the down
+//      matrices restricted to the slice's columns for a block of output rows,
+//      all slots summed;
+//   C. the XCD partials of a row block meet in the workspace; the XCD that
+//      arrives last (a counter per row block) adds the n_xcd partials in XCD
+//      order and writes the output.  In shard mode with one or more shards per
+//      XCD, the shard sums are written directly instead.
+// Producer/consumer traffic between workgroups uses write-through stores,
+// device-coherent atomics and cache-bypassing loads, never a device-scope
+// fence (those serialise across the chip).  Waits are bounded (kFuSpin); a
+// timeout sets DUCKMOE_STATUS_TIMEOUT.  Every counter is back at zero when the
+// launch ends, so a zero-filled workspace stays valid from call to call.
+#ifndef DUCKMOE_FU_WAVES
+#define DUCKMOE_FU_WAVES 8
+#endif
+constexpr int kFuSpin = 1 << 22;
+constexpr size_t kFuDoneOff = 256;     // uint32 doneA[x] at 256 + 128 x
+constexpr size_t kFuPassOff = 1280;    // uint32 passed[x] at 1280 + 128 x
+constexpr size_t kFuCntOff = 8192;     // uint32 cnt[r] at 8192 + 64 r
+constexpr int kFuMaxXcd = 8;
+constexpr int kFuMaxBlocks = 128;      // row blocks (workgroups per XCD)
+
+struct FuArgs {
+  uint8_t *hdr;   // workspace header
+  float *Y;       // [n_xcd][T][H] XCD partials
+  int n_xcd;
+  int G;          // lanes per reduction group in B (lane groups of one shard, or of one row)
+};
+
+// Phase timestamps (s_memrealtime, 100 MHz) per workgroup, for profiling builds
+// only (-DDUCKMOE_FU_TRACE): 8 x u64 per workgroup after the workspace's end.
+#ifdef DUCKMOE_FU_TRACE
+#define FU_MARK(f, i)                                                                   \
+  do {                                                                                \
+    if (threadIdx.x == 0)                                                             \
+      reinterpret_cast<unsigned long long *>((f).Y + (size_t)kFuMaxXcd * a.T * a.H)[  \
+          blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime();                   \
+  } while (0)
+#else
+#define FU_MARK(f, i) do { } while (0)
+#endif
+
+__device__ __forceinline__ uint32_t *fu_done(const FuArgs &f, int x) {
+  return reinterpret_cast<uint32_t *>(f.hdr + kFuDoneOff + 128 * x);
+}
+__device__ __forceinline__ uint32_t *fu_pass(const FuArgs &f, int x) {
+  return reinterpret_cast<uint32_t *>(f.hdr + kFuPassOff + 128 * x);
+}
+__device__ __forceinline__ uint32_t *fu_cnt(const FuArgs &f, int r) {
+  return reinterpret_cast<uint32_t *>(f.hdr + kFuCntOff + 64 * r);
+}
+__device__ __forceinline__ void st_through(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float ld_through(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t ld_ctr(uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_ctr(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_ctr(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// h' of one (slot, row) from the reduced gate/up sums
+__device__ __forceinline__ float swiglu_w(float wt, float g, float v) {
+  return (wt == 0.0f) ? 0.0f : wt * (silu(g) * v);
+}
+
+// B unit: M row groups of RPU rows (one slot's down matrix, the XCD slice's
+// columns).  Lane l covers rows q*M*RPU + m*RPU + l / LR (m < M) and the 16
+// columns at (l % LR) * 16 of the slice.
+#ifndef DUCKMOE_FU_BROWS
+#define DUCKMOE_FU_BROWS 4  // M: row groups per lane per B unit
+#endif
+template <int M>
+struct FbTile {
+  uint4 d[M];
+  uint32_t s[M];
+};
+
+template <int M>
+__device__ __forceinline__ void fb_issue(FbTile<M> &b, const LayerArgs &a,
+                                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rs,
+                                         int q, int RPU, int LR, uint32_t kx, int lane) {
+  const uint32_t H = a.H, I = a.I;
+  const uint32_t k = kx + (uint32_t)(lane % LR) * 16;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t row = (uint32_t)((q * M + m) * RPU + lane / LR);
+    const bool ok = row < H;
+    b.d[m] = buf_load16(rb, ok ? row * I + k : kOutOfRange);
+    b.s[m] = buf_load2(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
+  }
+}
+
+template <int T, int M>
+__device__ __forceinline__ void fb_consume(const FbTile<M> &b, const float *hs, int Ix, int slot,
+                                           int LR, int lane, float (&acc)[M][T][2]) {
+  float xv[T][16];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float4 *src =
+        reinterpret_cast<const float4 *>(hs + (slot * T + t) * Ix + (lane % LR) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = src[j];
+      xv[t][4 * j] = v.x; xv[t][4 * j + 1] = v.y; xv[t][4 * j + 2] = v.z; xv[t][4 * j + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    h2_t h[8];
+    fp9_decode16(b.d[m], b.s[m], h);
+#pragma unroll
+    for (int t = 0; t < T; ++t) fma16(h, xv[t], acc[m][t][0], acc[m][t][1]);
+  }
+}
+
+__device__ __forceinline__ float fb_reduce(float v, int G) {
+  switch (G) {
+    case 4: return group_sum<4>(v);
+    case 8: return group_sum<8>(v);
+    case 16: return group_sum<16>(v);
+    case 32: return group_sum<32>(v);
+    default: return group_sum<64>(v);
+  }
+}
+
+// A cursor over (row pair, chunk) units; pr = pair index within the XCD's list
+// (slot-major), ris = row of the pair inside its slot's slice.
+struct FaCur {
+  int u, pr, c, slot, ris;
+};
+
+__device__ __forceinline__ void fa_rsrc(const LayerArgs &a, const PlanLds &plan, int slot,
+                                        __amdgpu_buffer_rsrc_t &rb, __amdgpu_buffer_rsrc_t &rs) {
+  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+  const uint32_t mat = (uint32_t)a.I * (uint32_t)a.H;
+  rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
+  rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
+}
+
+template <int T, int WA>
+__global__ __launch_bounds__(WA * 64) void k_fused(const LayerArgs a, const FuArgs f) {
+  constexpr int M = DUCKMOE_FU_BROWS;
+  __shared__ PlanLds plan;
+  __shared__ int meta[WA][2];            // pair / row-block index of each wave's split ends
+  __shared__ float pa[WA][2][T][2];      // A split partials (g, v)
+  __shared__ float pb[WA][2][M][T][16];  // B split partials (64 / G groups per row group)
+  __shared__ uint32_t bcast;
+  extern __shared__ float4 lds4[];       // xs [T][Hp] | hs [S][T][Ix]
+  constexpr int NT = WA * 64;
+  constexpr int XR = 8;
+  const int H = a.H, I = a.I, H4 = a.H / 4;
+  const int nc = (H + kChunk - 1) / kChunk;
+  const int Hp4 = nc * (kChunk / 4);
+  const int n4 = T * Hp4;
+  const float4 *xg = reinterpret_cast<const float4 *>(a.x);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  FU_MARK(f, 0);
+
+  // ---- prologue: ids, then x loads overlapping the plan; x into LDS
+  const PlanIn pin = plan_load(a);
+  float4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int q = threadIdx.x + j * NT;
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    xr[j] = (q < n4 && k4 < H4) ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  build_plan(plan, a, pin, reinterpret_cast<uint32_t *>(lds4),
+             reinterpret_cast<int *>(lds4) + kMaxWords);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hdr->status = plan.status;
+    a.hdr->n_slots = plan.n_slots;
+  }
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int q = threadIdx.x + j * NT;
+    if (q < n4) lds4[q] = xr[j];
+  }
+  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) {
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    lds4[q] = k4 < H4 ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (threadIdx.x < 2 * WA) (&meta[0][0])[threadIdx.x] = -1;
+  __syncthreads();
+  FU_MARK(f, 1);
+
+  const int S = plan.n_slots;
+  const int nx = f.n_xcd;
+  const int xcd = blockIdx.x % nx;
+  const int r = blockIdx.x / nx;
+  const int Gx = gridDim.x / nx;
+  const int Ix = I / nx;
+  const uint32_t kx = (uint32_t)xcd * Ix;
+  float *hs = reinterpret_cast<float *>(lds4 + n4);
+
+  // ---- A: gate/up pairs of this XCD's slice
+  {
+    const int PT = S * Ix;
+    const int p0 = (int)((long)r * PT / Gx), p1 = (int)((long)(r + 1) * PT / Gx);
+    const int U = (p1 - p0) * nc;
+    const int u0 = (int)((long)wave * U / WA), u1 = (int)((long)(wave + 1) * U / WA);
+    float acc[2][1][T][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[g][0][t][0] = acc[g][0][t][1] = 0.0f;
+    // at the last unit of a pair, or of the range: reduce, then finish or park
+    auto pair_end = [&](const FaCur &cu) {
+      const bool whole_start = cu.u - cu.c >= u0;  // the pair's chunk 0 is in range
+      const bool done = cu.c == nc - 1;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float gs = wave_sum(acc[0][0][t][0] + acc[0][0][t][1]);
+        const float vs = wave_sum(acc[1][0][t][0] + acc[1][0][t][1]);
+        acc[0][0][t][0] = acc[0][0][t][1] = acc[1][0][t][0] = acc[1][0][t][1] = 0.0f;
+        if (lane == 0) {
+          if (whole_start && done) {
+            st_through(a.hbuf + ((size_t)cu.slot * T + t) * I + kx + cu.ris,
+                       swiglu_w(plan.w[cu.slot][t], gs, vs));
+          } else {
+            pa[wave][whole_start ? 1 : 0][t][0] = gs;
+            pa[wave][whole_start ? 1 : 0][t][1] = vs;
+          }
+        }
+      }
+      if (!(whole_start && done) && lane == 0) meta[wave][whole_start ? 1 : 0] = cu.pr;
+    };
+    if (u0 < u1) {
+      FaCur cur;
+      cur.u = u0;
+      cur.pr = p0 + u0 / nc;
+      cur.c = u0 - (cur.pr - p0) * nc;
+      cur.slot = cur.pr / Ix;
+      cur.ris = cur.pr - cur.slot * Ix;
+      __amdgpu_buffer_rsrc_t rb, rs;
+      fa_rsrc(a, plan, cur.slot, rb, rs);
+      auto unit = [&](const FaCur &cu) {
+        GuUnit un;
+        un.rb = rb;
+        un.rs = rs;
+        un.row0 = kx + (uint32_t)cu.ris;
+        un.kc = (uint32_t)cu.c * kChunk;
+        return un;
+      };
+      auto advance = [&](FaCur &cu) {
+        ++cu.u;
+        if (++cu.c == nc) {
+          cu.c = 0;
+          ++cu.pr;
+          if (++cu.ris == Ix) {
+            cu.ris = 0;
+            ++cu.slot;
+            if (cu.u < u1) fa_rsrc(a, plan, cu.slot, rb, rs);
+          }
+        }
+      };
+      GuTile<1> b0, b1;
+      FaCur c0 = cur, c1;
+      gu_issue(b0, unit(c0), a, lane);
+      while (true) {
+        c1 = c0;
+        advance(c1);
+        if (c1.u < u1) gu_issue(b1, unit(c1), a, lane);
+        gu_consume<T, 1>(b0, lds4, Hp4, (uint32_t)c0.c * kChunk, lane, acc);
+        if (c0.c == nc - 1 || c0.u + 1 == u1) pair_end(c0);
+        if (c1.u >= u1) break;
+        c0 = c1;
+        advance(c0);
+        if (c0.u < u1) gu_issue(b0, unit(c0), a, lane);
+        gu_consume<T, 1>(b1, lds4, Hp4, (uint32_t)c1.c * kChunk, lane, acc);
+        if (c1.c == nc - 1 || c1.u + 1 == u1) pair_end(c1);
+        if (c0.u >= u1) break;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  FU_MARK(f, 2);
+  // pairs split between waves: sum the parts in wave order, then finish
+  if (threadIdx.x < 2 * WA) {
+    const int w = threadIdx.x >> 1, side = threadIdx.x & 1;
+    const int pr = meta[w][side];
+    bool first = pr >= 0;
+    for (int w2 = 0; w2 <= w && first; ++w2)
+      for (int s2 = 0; s2 < 2; ++s2)
+        if ((w2 < w || s2 < side) && meta[w2][s2] == pr) first = false;
+    if (first) {
+      const int slot = pr / Ix;
+      for (int t = 0; t < T; ++t) {
+        float gs = 0.0f, vs = 0.0f;
+        for (int w2 = 0; w2 < WA; ++w2)
+          for (int s2 = 0; s2 < 2; ++s2)
+            if (meta[w2][s2] == pr) { gs += pa[w2][s2][t][0]; vs += pa[w2][s2][t][1]; }
+        st_through(a.hbuf + ((size_t)slot * T + t) * I + kx + (pr - slot * Ix),
+                   swiglu_w(plan.w[slot][t], gs, vs));
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < 2 * WA) (&meta[0][0])[threadIdx.x] = -1;
+
+  // ---- B setup: this workgroup's row blocks; first unit in flight during the wait
+  const int LR = Ix / 16;          // lanes per row
+  const int RPU = 64 / LR;         // rows per row group
+  const int nq = (H + M * RPU - 1) / (M * RPU);
+  const int q0 = (int)((long)r * nq / Gx), q1 = (int)((long)(r + 1) * nq / Gx);
+  const int UB = (q1 - q0) * S;
+  const int ub0 = (int)((long)wave * UB / WA), ub1 = (int)((long)(wave + 1) * UB / WA);
+  const uint32_t dmat = (uint32_t)H * (uint32_t)I;
+  auto drsrc = [&](int slot, __amdgpu_buffer_rsrc_t &rb, __amdgpu_buffer_rsrc_t &rs) {
+    const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
+    rb = make_rsrc(a.dn_body + (size_t)e * dmat, dmat);
+    rs = make_rsrc(a.dn_sign + (size_t)e * (dmat / 8), dmat / 8);
+  };
+  FbTile<M> t0, t1;
+  int bq = 0, bs = 0;  // B cursor: row block, slot
+  if (ub0 < ub1) {
+    bq = q0 + ub0 / S;
+    bs = ub0 - (bq - q0) * S;
+    __amdgpu_buffer_rsrc_t rb, rs;
+    drsrc(bs, rb, rs);
+    fb_issue<M>(t0, a, rb, rs, bq, RPU, LR, kx, lane);
+  }
+
+  // ---- wait for the XCD's A phase; stage its h' slice
+  if (threadIdx.x == 0) {
+    add_ctr(fu_done(f, xcd), 1u);
+    int it = 0;
+    while (ld_ctr(fu_done(f, xcd)) < (uint32_t)Gx && it < kFuSpin) {
+      __builtin_amdgcn_s_sleep(2);
+      ++it;
+    }
+    if (it >= kFuSpin) atomicOr(&a.hdr->status, DUCKMOE_STATUS_TIMEOUT);
+  }
+  __syncthreads();
+  FU_MARK(f, 3);
+  if (threadIdx.x == 0) {
+    if (add_ctr(fu_pass(f, xcd), 1u) == (uint32_t)Gx - 1) {  // everyone is past the wait
+      st_ctr(fu_done(f, xcd), 0u);
+      st_ctr(fu_pass(f, xcd), 0u);
+    }
+  }
+  for (int q = threadIdx.x; q < S * T * Ix; q += NT) {
+    const int st = q / Ix, i = q - st * Ix;  // st = slot * T + t
+    hs[q] = ld_through(a.hbuf + (size_t)st * I + kx + i);
+  }
+  __syncthreads();
+  FU_MARK(f, 4);
+
+  // ---- B: down rows x slice columns, all slots; units (row block q, slot s)
+  const int G = f.G;               // lanes per reduction group
+  const int ns = a.n_shards;
+  {
+    float acc[M][T][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[m][t][0] = acc[m][t][1] = 0.0f;
+    auto emit = [&](int row, int t, int lanepos, float v) {
+      if (row >= H) return;
+      if (ns == 1) {
+        st_through(f.Y + ((size_t)xcd * T + t) * H + row, v);
+      } else {
+        const int shard = (int)((kx + (lanepos % LR) / G * G * 16) / (uint32_t)(I / ns));
+        a.out[((size_t)shard * T + t) * H + row] = v;
+      }
+    };
+    // after the last slot of a row block, or at the end of the range
+    auto block_end = [&](int u, int q, int sl) {
+      const bool whole_start = u - sl >= ub0;
+      const bool done = sl == S - 1;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float v = fb_reduce(acc[m][t][0] + acc[m][t][1], G);
+          acc[m][t][0] = acc[m][t][1] = 0.0f;
+          if ((lane & (G - 1)) == G - 1) {
+            if (whole_start && done)
+              emit((q * M + m) * RPU + lane / LR, t, lane, v);
+            else
+              pb[wave][whole_start ? 1 : 0][m][t][lane / G] = v;
+          }
+        }
+      if (!(whole_start && done) && lane == 0) meta[wave][whole_start ? 1 : 0] = q;
+    };
+    if (ub0 < ub1) {
+      __amdgpu_buffer_rsrc_t rb, rs;
+      int u = ub0, q = bq, sl = bs;
+      while (true) {
+        // next unit's cursor
+        int q1n = q, s1n = sl + 1;
+        if (s1n == S) { s1n = 0; ++q1n; }
+        if (u + 1 < ub1) { drsrc(s1n, rb, rs); fb_issue<M>(t1, a, rb, rs, q1n, RPU, LR, kx, lane); }
+        fb_consume<T, M>(t0, hs, Ix, sl, LR, lane, acc);
+        if (sl == S - 1 || u + 1 == ub1) block_end(u, q, sl);
+        if (++u >= ub1) break;
+        q = q1n; sl = s1n;
+        int q2n = q, s2n = sl + 1;
+        if (s2n == S) { s2n = 0; ++q2n; }
+        if (u + 1 < ub1) { drsrc(s2n, rb, rs); fb_issue<M>(t0, a, rb, rs, q2n, RPU, LR, kx, lane); }
+        fb_consume<T, M>(t1, hs, Ix, sl, LR, lane, acc);
+        if (sl == S - 1 || u + 1 == ub1) block_end(u, q, sl);
+        if (++u >= ub1) break;
+        q = q2n; sl = s2n;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  FU_MARK(f, 5);
+  // row blocks split between waves: sum the parts in wave order
+  for (int e = threadIdx.x; e < 2 * WA * 64; e += NT) {
+    const int ws = e / 64, ln = e % 64;  // (wave, side) entry, lane position
+    const int w = ws >> 1, side = ws & 1;
+    const int q = meta[w][side];
+    if (q < 0 || (ln & (G - 1)) != G - 1) continue;
+    bool first = true;
+    for (int w2 = 0; w2 <= w && first; ++w2)
+      for (int s2 = 0; s2 < 2; ++s2)
+        if ((w2 < w || s2 < side) && meta[w2][s2] == q) first = false;
+    if (!first) continue;
+    for (int m = 0; m < M; ++m) {
+      const int row = (q * M + m) * RPU + ln / LR;
+      if (row >= H) continue;
+      for (int t = 0; t < T; ++t) {
+        float v = 0.0f;
+        for (int w2 = 0; w2 < WA; ++w2)
+          for (int s2 = 0; s2 < 2; ++s2)
+            if (meta[w2][s2] == q) v += pb[w2][s2][m][t][ln / G];
+        if (ns == 1) {
+          st_through(f.Y + ((size_t)xcd * T + t) * H + row, v);
+        } else {
+          const int shard = (int)((kx + (ln % LR) / G * G * 16) / (uint32_t)(I / ns));
+          a.out[((size_t)shard * T + t) * H + row] = v;
+        }
+      }
+    }
+  }
+  if (ns != 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- C: the last XCD to finish this row range adds the partials in XCD order
+  FU_MARK(f, 6);
+  if (threadIdx.x == 0) bcast = add_ctr(fu_cnt(f, r), 1u);
+  __syncthreads();
+  if (bcast != (uint32_t)nx - 1) return;
+  const int row_lo = q0 * M * RPU, row_hi = min(q1 * M * RPU, H);
+  for (int q = threadIdx.x; q < (row_hi - row_lo) * T; q += NT) {
+    const int t = q / (row_hi - row_lo), row = row_lo + q % (row_hi - row_lo);
+    float v = 0.0f;
+    for (int x2 = 0; x2 < nx; ++x2) v += ld_through(f.Y + ((size_t)x2 * T + t) * H + row);
+    a.out[(size_t)t * H + row] = v;
+  }
+  if (threadIdx.x == 0) st_ctr(fu_cnt(f, r), 0u);
+  FU_MARK(f, 7);
+}
+
 // ------------------------------------------------------ building blocks ----
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ body,
                                                 const uint8_t *__restrict__ sign, int64_t n,
@@ -602,7 +1111,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ body,
 __global__ __launch_bounds__(64) void k_plan(const LayerArgs a, int32_t *uniq, int32_t *n_slots) {
   __shared__ PlanLds plan;
   __shared__ uint32_t scratch[2 * kMaxWords];
-  build_plan(plan, a, scratch, reinterpret_cast<int *>(scratch) + kMaxWords);
+  build_plan(plan, a, plan_load(a), scratch, reinterpret_cast<int *>(scratch) + kMaxWords);
   for (int s = threadIdx.x; s < plan.n_slots; s += blockDim.x) uniq[s] = plan.expert[s];
   if (threadIdx.x == 0) *n_slots = plan.n_slots;
 }
@@ -653,8 +1162,14 @@ size_t hbuf_slots(const duckmoe_layer *L, int T, bool single) {
   return single ? 1 : (size_t)T * L->top_k + 1;
 }
 
+size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
+  return hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
+}
+
+// header | h' [slots][T][I] | XCD partials [kFuMaxXcd][T][H] (fused path)
 size_t ws_need(const duckmoe_layer *L, int T, bool single) {
-  return kHdrBytes + hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
+  return kHdrBytes + hbuf_bytes(L, T, single) +
+         (size_t)kFuMaxXcd * T * L->hidden * sizeof(float);
 }
 
 // Launch shape of the down kernel (compile-time; defaults measured on MI355X).
@@ -662,10 +1177,10 @@ size_t ws_need(const duckmoe_layer *L, int T, bool single) {
 #define DUCKMOE_DN_WAVES 2          // waves per workgroup
 #endif
 #ifndef DUCKMOE_DN_ROWS
-#define DUCKMOE_DN_ROWS 4           // output rows per block at T = 1 (see down_rows)
+#define DUCKMOE_DN_ROWS 7           // output rows per block at T = 1 (see down_rows)
 #endif
 #ifndef DUCKMOE_DN_WAVES_PER_CU
-#define DUCKMOE_DN_WAVES_PER_CU 8   // target resident waves per CU (capped by occupancy)
+#define DUCKMOE_DN_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
 #endif
 constexpr int kWB = DUCKMOE_DN_WAVES;
 
@@ -715,8 +1230,7 @@ template <int T>
 hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
   constexpr int R = down_rows<T>();
   const auto kern = k_down<T, R, kWB>;
-  const size_t lds = std::max((size_t)kWB * R * T * 16 * sizeof(float),
-                              (size_t)2 * kMaxWords * 4);
+  const size_t lds = (size_t)kWB * R * T * 16 * sizeof(float);
   int per_cu = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWB * 64, lds);
   if (err != hipSuccess) return err;
@@ -758,6 +1272,69 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
   }
 }
 
+#ifndef DUCKMOE_FU_WAVES_PER_CU
+#define DUCKMOE_FU_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+#ifndef DUCKMOE_FU_COOPERATIVE
+#define DUCKMOE_FU_COOPERATIVE 0    // 1: cooperative launch (co-residency guaranteed, ~17 us slower)
+#endif
+#ifndef DUCKMOE_FUSED
+#define DUCKMOE_FUSED 0             // 1: single-launch layer for T <= 2 (slower than two launches
+                                    //    as measured on MI355X; kept for experiments)
+#endif
+
+// Logical XCDs the fused kernel splits the intermediate dimension over: the
+// chip's 8 when the device is a whole MI355X (256 CUs, 32 per XCD).  Any value
+// is correct; it only decides locality and balance.
+int fused_xcds(int cus) { return (cus >= 64 && cus % 8 == 0) ? 8 : 1; }
+
+// The fused kernel's LDS: x [T][Hp] + the XCD's h' slice [slots][T][Ix].
+size_t fused_lds(const LayerArgs &a, int slots, int nx) {
+  const size_t hp = (size_t)((a.H + kChunk - 1) / kChunk) * kChunk;
+  return (size_t)a.T * hp * sizeof(float) + (size_t)slots * a.T * (a.I / nx) * sizeof(float);
+}
+
+bool fused_ok(const LayerArgs &a, int slots, int nx) {
+  if (a.T > 2 || a.I % nx) return false;
+  const int ix = a.I / nx;
+  if (ix < 64 || ix > 1024 || (ix & (ix - 1))) return false;
+  if (a.n_shards != 1) {
+    const int w = a.I / a.n_shards;  // a power of two in [64, 1024] (check_shards)
+    if (w > ix) return false;       // a shard spanning XCDs needs a cross-XCD reduce
+  }
+  return fused_lds(a, slots, nx) <= 150 * 1024;
+}
+
+template <int T>
+hipError_t launch_fused_t(const LayerArgs &a, int slots, int nx, FuArgs f, hipStream_t st) {
+  constexpr int WA = DUCKMOE_FU_WAVES;
+  const auto kern = k_fused<T, WA>;
+  const size_t lds = fused_lds(a, slots, nx);
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  int per_cu = 0;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WA * 64, lds);
+  if (err != hipSuccess) return err;
+  const int cus = device_cus();
+  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  per_cu = std::max(1, std::min(per_cu, DUCKMOE_FU_WAVES_PER_CU / WA));
+  int grid = cus * per_cu;
+  grid -= grid % nx;
+  if (grid / nx > kFuMaxBlocks) grid = kFuMaxBlocks * nx;
+  const int ix = a.I / nx;
+  f.G = (a.n_shards == 1) ? ix / 16 : (a.I / a.n_shards) / 16;
+  f.n_xcd = nx;
+  if (DUCKMOE_FU_COOPERATIVE) {
+    LayerArgs aa = a;
+    void *args[] = {&aa, &f};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern), dim3(grid),
+                                      dim3(WA * 64), args, (unsigned)lds, st);
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), lds, st, a, f);
+  return hipGetLastError();
+}
+
 enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
 
 // Shared argument checks and dispatch of the layer entry points.
@@ -796,6 +1373,19 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   a.hdr = reinterpret_cast<WsHeader *>(ws);
   a.hbuf = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes);
 
+  if (DUCKMOE_FUSED && stages == kBoth) {
+    const int slots = (int)hbuf_slots(L, T, single);
+    const int nx = fused_xcds(device_cus());
+    if (fused_ok(a, slots, nx)) {
+      FuArgs f;
+      f.hdr = reinterpret_cast<uint8_t *>(ws);
+      f.Y = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes +
+                                      hbuf_bytes(L, T, single));
+      const hipError_t err = T == 1 ? launch_fused_t<1>(a, slots, nx, f, stream)
+                                    : launch_fused_t<2>(a, slots, nx, f, stream);
+      return err == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+    }
+  }
   if (stages & kGateUp) {
     if (launch_gate_up(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   }

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libduckmoe.so")
 
 OK, EINVAL, ESHAPE, ENONFINITE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
-STATUS_BAD_ID, STATUS_DUP_ID = 1, 2
+STATUS_BAD_ID, STATUS_DUP_ID, STATUS_TIMEOUT = 1, 2, 4
 MAX_TOKENS = 8
 
 _lib = None
@@ -200,8 +200,9 @@ class Layer:
         return n
 
     def workspace(self, T, n_shards=1):
+        """A zero-filled device workspace (the library needs it zeroed once)."""
         import torch
-        return torch.empty(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
+        return torch.zeros(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
                            device=self.gu_body.device)
 
 

@@ -54,6 +54,8 @@ extern "C" {
 /* Bits of the device status word (duckmoe_status). */
 #define DUCKMOE_STATUS_BAD_ID  1  /* a routed id outside [0, n_routed): entry skipped   */
 #define DUCKMOE_STATUS_DUP_ID  2  /* a token lists an id twice: its weights were added  */
+#define DUCKMOE_STATUS_TIMEOUT 4  /* a bounded in-kernel wait expired: output invalid;
+                                     zero-fill the workspace before reusing it         */
 
 #define DUCKMOE_MAX_TOKENS 8      /* T, tokens per call                                 */
 #define DUCKMOE_MAX_IDS    64     /* T * top_k                                          */
@@ -105,8 +107,11 @@ int duckmoe_quantize_fp9(const float *w, int64_t rows, int64_t cols,
 /*
  * Bytes of device workspace duckmoe_expert_ffn / duckmoe_moe_layer need for T
  * tokens (the same figure covers both).  Returns 0 if the arguments are
- * invalid.  The workspace holds the expert-selection plan, the status word and
- * the per-(expert, token) SwiGLU activations (f32).
+ * invalid.  The workspace holds the status word, synchronisation counters, the
+ * per-(expert, token) SwiGLU activations (f32) and per-XCD partial outputs.
+ * A workspace must be zero-filled once before its first use; every call leaves
+ * its counters at zero again.  Calls that may run at the same time need
+ * separate workspaces.
  */
 size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shards);
 

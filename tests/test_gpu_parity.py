@@ -126,6 +126,10 @@ SMALL = [
     # (workload, H, I, n_routed, top_k): ragged last chunk in both GEMVs
     (100, 1040, 336, 24, 8),
     (101, 2064, 1536, 16, 4),
+    # intermediate sizes whose per-XCD slice is a power of two (single-launch
+    # path at T <= 2): slices of 64 and 128 columns, ragged hidden chunk
+    (102, 1040, 512, 20, 8),
+    (103, 2064, 1024, 12, 6),
 ]
 
 
@@ -146,13 +150,15 @@ def run_layer_case(torch, lay, ox, wl, step, T, n_shards=1, ids=None, w=None):
         ids, w = synth.routing(SEED, wl, 0, step, T, lay.n_routed, lay.top_k)
     valid = ids[(ids >= 0) & (ids < lay.n_routed)]
     ox.prefetch(list(valid) + [lay.n_routed])
+    ws = lay.workspace(T, n_shards)
     out = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids.astype(np.int32)),
-                       to_dev(torch, w.astype(np.float32)), n_shards=n_shards)
+                       to_dev(torch, w.astype(np.float32)), n_shards=n_shards, ws=ws)
     torch.cuda.synchronize()
+    assert dm.status(ws) & dm.duckmoe.STATUS_TIMEOUT == 0
     return x, ids, w, out.cpu().numpy()
 
 
-@pytest.mark.parametrize("wl", [100, 101])
+@pytest.mark.parametrize("wl", [100, 101, 102, 103])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_small_layer_all_batch_sizes(torch_dev, small_layers, wl, T):
     torch = torch_dev
@@ -163,6 +169,30 @@ def test_small_layer_all_batch_sizes(torch_dev, small_layers, wl, T):
     x, ids, w, got = run_layer_case(torch, lay, ox, wl, T, T)
     ref = oracle.moe_layer(ox, x, ids, w, lay.n_routed)
     check_close(got, ref, "layer %d T=%d" % (wl, T))
+
+
+@pytest.mark.parametrize("n_shards", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 2])
+def test_small_layer_fused_shards(torch_dev, small_layers, n_shards, T):
+    """I = 1024 split 8 ways (128-column slices): shards of 512 / 256 span
+    several slices (two-launch path), 128 / 64 lie inside one."""
+    torch = torch_dev
+    lay, ox = small_layers[103]
+    say("fused-size layer, T =", T, "n_shards =", n_shards)
+    ws = lay.workspace(T, n_shards)
+    x = synth.activations(SEED, 103, 0, 300 + n_shards, T, lay.hidden)
+    ids, w = synth.routing(SEED, 103, 0, 300 + n_shards, T, lay.n_routed, lay.top_k)
+    ox.prefetch(list(ids.ravel()) + [lay.n_routed])
+    for rep in range(2):  # the second call reuses the workspace's counters
+        got = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w),
+                           n_shards=n_shards, ws=ws).cpu().numpy()
+        assert dm.status(ws) == 0
+        if n_shards == 1:
+            check_close(got, oracle.moe_layer(ox, x, ids, w, lay.n_routed), "fused T=%d" % T)
+        else:
+            ref = oracle.moe_partials(ox, x, ids, w, lay.n_routed, n_shards)
+            for r in range(n_shards):
+                check_close(got[r], ref[r], "fused shard %d/%d" % (r, n_shards))
 
 
 @pytest.mark.parametrize("n_shards", [2, 3, 6, 12, 24])
@@ -248,7 +278,9 @@ def test_zero_weights_and_stage_split(torch_dev, small_layers):
     ws2 = lay.workspace(2)
     dm.moe_gate_up(lay, xd, idd, wd, ws2)
     split = dm.moe_down(lay, xd, idd, wd, ws2).cpu().numpy()
-    np.testing.assert_array_equal(full, split)
+    check_close(split, full, "stage split vs one call")
+    ox.prefetch(list(ids.ravel()) + [E])
+    check_close(split, oracle.moe_layer(ox, x, ids, w, E), "stage split")
 
 
 def test_repeat_calls_bit_identical(torch_dev, small_layers):
