@@ -47,10 +47,8 @@ namespace {
 
 constexpr int kMaxT = DUCKMOE_MAX_TOKENS;
 constexpr int kMaxIds = DUCKMOE_MAX_IDS;
-constexpr int kMaxSlots = kMaxIds + 1;
-constexpr int kMaxWords = DUCKMOE_MAX_ROUTED / 32;
 constexpr int kChunk = 1024;          // weights per wave-row step: 64 lanes x 16
-constexpr size_t kHdrBytes = 16384;   // workspace header (status, plan size, fused-path counters)
+constexpr size_t kHdrBytes = 1024;    // workspace header (status word, plan)
 
 // Launch shape of the gate/up kernel (compile-time; defaults measured on MI355X).
 #ifndef DUCKMOE_GU_WAVES
@@ -59,11 +57,14 @@ constexpr size_t kHdrBytes = 16384;   // workspace header (status, plan size, fu
 #ifndef DUCKMOE_GU_PAIRS
 #define DUCKMOE_GU_PAIRS 1     // (gate, up) row pairs per wave task
 #endif
-#ifndef DUCKMOE_GU_PREFETCH
-#define DUCKMOE_GU_PREFETCH 1  // 1: next chunk's loads in flight while computing
+#ifndef DUCKMOE_GU_DEPTH
+#define DUCKMOE_GU_DEPTH 3     // units whose loads a wave keeps in flight (2 or 3)
 #endif
 #ifndef DUCKMOE_GU_WAVES_PER_CU
 #define DUCKMOE_GU_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+#ifndef DUCKMOE_GU_MAP
+#define DUCKMOE_GU_MAP 0
 #endif
 constexpr int kGuTokens = 4;   // tokens per gate/up pass (x of all of them sits in LDS)
 
@@ -74,7 +75,7 @@ struct WsHeader {
   int32_t status;
   int32_t n_slots;
 };
-constexpr size_t kPlanOff = 4096;
+constexpr size_t kPlanOff = 256;   // int32 n_slots, then expert[slot]
 
 struct LayerArgs {
   int H, I, n_routed, top_k, T, n_shards;
@@ -89,106 +90,120 @@ struct LayerArgs {
 };
 
 // ----------------------------------------------------------------- plan ----
-// Expert-selection plan, built by every workgroup from the <= 64 routed ids:
-// slots 0..n-1 are the ascending distinct valid ids, slot n is the shared
-// expert (index n_routed, weight 1).  w[slot][t] is token t's routing weight
-// for the slot (summed over repeats, 0 if the token does not use it).
-struct PlanLds {
-  int n_slots;
-  int status;
-  int expert[kMaxSlots];
-  float w[kMaxSlots][kMaxT];
-  int id[kMaxIds];      // the routed ids and weights, staged for the loops below
-  float wi[kMaxIds];
-};
-
-// Thread tid < T * top_k loads its id and weight before anything else, so that
-// the plan's first global round trip is not queued behind other loads.
+// Expert-selection plan.  Every wave builds it on its own from the <= 64
+// routed ids, one per lane, with cross-lane operations only (no LDS, no
+// barrier).  Slot 0 is the shared expert (index n_routed), or the one expert
+// of single-expert mode; slots 1 .. n_slots-1 are the distinct valid ids in
+// order of first appearance (token-major).  Slot 0 needs no ids, so work on it
+// can start before they arrive.  A token's weight for a routed slot is the sum
+// of its weights at the positions naming that expert (0 if none); its weight
+// for slot 0 is 1.
 struct PlanIn {
   int id;
   float w;
 };
 
+// Lane j < T * top_k loads position j's id and weight.  Unconditional buffer
+// loads (lanes past the end read zero): a branch around a load makes the
+// compiler drain every earlier load first.
 __device__ __forceinline__ PlanIn plan_load(const LayerArgs &a) {
-  PlanIn in{-1, 0.0f};
-  const int tid = threadIdx.x;
-  if (a.ids != nullptr && tid < a.T * a.top_k) {
-    in.id = a.ids[tid];
-    if (a.w != nullptr) in.w = a.w[tid];
-  }
+  const uint32_t n = a.ids != nullptr ? (uint32_t)(a.T * a.top_k) : 0u;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t off = lane < n ? lane * 4u : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.ids, n * 4u);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w != nullptr ? n * 4u : 0u);
+  PlanIn in;
+  in.id = (int)buf_load4(ri, off);
+  in.w = __builtin_bit_cast(float, buf_load4(rw, off));
   return in;
 }
 
-// bitmap/prefix: 2 * kMaxWords words of scratch LDS, free again on return.
-__device__ void build_plan(PlanLds &P, const LayerArgs &a, const PlanIn in, uint32_t *bitmap,
-                           int *prefix) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  if (a.ids == nullptr) {
-    if (tid == 0) {
-      P.n_slots = 1;
-      P.status = 0;
-      P.expert[0] = a.single_expert;
-    }
-    if (tid < kMaxT) P.w[0][tid] = 1.0f;
-    __syncthreads();
-    return;
-  }
-  const int N = a.T * a.top_k;
-  const int nwords = (a.n_routed + 31) >> 5;
-  for (int i = tid; i < nwords; i += nt) bitmap[i] = 0u;
-  for (int i = tid; i < kMaxSlots * kMaxT; i += nt) (&P.w[0][0])[i] = 0.0f;
-  if (tid == 0) P.status = 0;
-  if (tid < N) {
-    P.id[tid] = in.id;
-    P.wi[tid] = in.w;
-  }
-  __syncthreads();
+struct WavePlan {
+  int n_slots;  // uniform
+  int status;   // uniform: DUCKMOE_STATUS_* bits
+  int e0;       // uniform: expert of slot 0
+  int slot;     // lane j < T * top_k: slot of position j, -1 if its id is invalid
+  float w;      // lane j: routing weight at position j
+  int expert;   // lane s < n_slots - 1: expert of slot s + 1
+};
 
+__device__ __forceinline__ int slot0_expert(const LayerArgs &a) {
+  return a.ids != nullptr ? a.n_routed : a.single_expert;
+}
+
+__device__ __forceinline__ WavePlan wave_plan(const LayerArgs &a, const PlanIn in) {
+  const int lane = threadIdx.x & 63;
+  WavePlan p;
+  p.e0 = slot0_expert(a);
+  if (a.ids == nullptr) {
+    p.n_slots = 1;
+    p.status = 0;
+    p.slot = -1;
+    p.w = 0.0f;
+    p.expert = 0;
+    return p;
+  }
+  const int N = a.T * a.top_k;  // <= 64
   const int id = in.id;
-  const bool valid = tid < N && id >= 0 && id < a.n_routed;
-  const int tok = tid < N ? tid / a.top_k : 0;
-  const int base = tok * a.top_k;
-  if (tid < N) {
-    int st = 0;
-    if (!valid) {
-      st |= DUCKMOE_STATUS_BAD_ID;
-    } else {
-      atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-      for (int j = base; j < tid; ++j)
-        if (P.id[j] == id) st |= DUCKMOE_STATUS_DUP_ID;
-    }
-    if (st) atomicOr(&P.status, st);
+  const bool valid = lane < N && id >= 0 && id < a.n_routed;
+  const int tok = lane / a.top_k;
+  // the earliest position with the same id, and repeats within one token
+  int firstk = lane;
+  bool dup = false;
+  for (int k = 0; k < N; ++k) {
+    const int idk = __builtin_amdgcn_readlane(id, k);
+    const bool same = valid && k < lane && idk == id;
+    if (same && firstk == lane) firstk = k;
+    if (same && k / a.top_k == tok) dup = true;
   }
-  __syncthreads();
-  for (int i = tid; i < nwords; i += nt) prefix[i] = __popc(bitmap[i]);
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nwords; ++i) {
-      const int c = prefix[i];
-      prefix[i] = run;
-      run += c;
-    }
-    P.n_slots = run + 1;
-    P.expert[run] = a.n_routed;
+  const bool first = valid && firstk == lane;
+  const uint64_t fmask = __builtin_amdgcn_ballot_w64(first);
+  const int before = (int)__builtin_amdgcn_mbcnt_hi(
+      (uint32_t)(fmask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)fmask, 0u));
+  // a first occurrence takes slot 1 + (first occurrences before it); a repeat
+  // takes its first occurrence's slot
+  const int s = __builtin_amdgcn_ds_bpermute(firstk * 4, 1 + before);
+  p.slot = valid ? s : -1;
+  p.w = lane < N ? in.w : 0.0f;
+  p.n_slots = 1 + (int)__builtin_popcountll(fmask);
+  // lane r receives the id of the r-th first occurrence; the other lanes send
+  // to lane 63, which holds a slot only when every position is a first one
+  p.expert = __builtin_amdgcn_ds_permute((first ? before : 63) * 4, id);
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(lane < N && !valid);
+  const uint64_t dups = __builtin_amdgcn_ballot_w64(dup);
+  p.status = (bad ? DUCKMOE_STATUS_BAD_ID : 0) | (dups ? DUCKMOE_STATUS_DUP_ID : 0);
+  return p;
+}
+
+// expert of slot s (s uniform, < n_slots)
+__device__ __forceinline__ int plan_expert(const WavePlan &p, int s) {
+  return s == 0 ? p.e0 : __builtin_amdgcn_readlane(p.expert, s - 1);
+}
+
+// token t's routing weight for slot s (s, t uniform)
+__device__ __forceinline__ float plan_weight(const WavePlan &p, const LayerArgs &a, int s, int t) {
+  if (s == 0) return 1.0f;
+  float wt = 0.0f;
+  for (int i = 0; i < a.top_k; ++i) {
+    const int j = t * a.top_k + i;
+    if (__builtin_amdgcn_readlane(p.slot, j) == s)
+      wt += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p.w), j));
   }
-  __syncthreads();
-  if (valid) {
-    const int wd = id >> 5;
-    const int slot = prefix[wd] + __popc(bitmap[wd] & ((1u << (id & 31)) - 1u));
-    P.expert[slot] = id;  // every lane holding this id writes the same value
-    bool first = true;
-    for (int j = base; j < tid; ++j)
-      if (P.id[j] == id) first = false;
-    if (first) {
-      float sum = 0.0f;
-      for (int j = base; j < base + a.top_k; ++j)
-        if (P.id[j] == id) sum += P.wi[j];
-      P.w[slot][tok] = sum;
-    }
+  return wt;
+}
+
+// The plan as the down launch reads it from the workspace: int32 n_slots, then
+// the expert of each slot.  Written by one wave.
+__device__ __forceinline__ void plan_store(const WavePlan &p, const LayerArgs &a) {
+  int32_t *dst = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(a.hdr) + kPlanOff);
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) {
+    a.hdr->status = p.status;
+    a.hdr->n_slots = p.n_slots;
+    dst[0] = p.n_slots;
+    dst[1] = p.e0;
   }
-  if (tid < a.T) P.w[P.n_slots - 1][tid] = 1.0f;
-  __syncthreads();
+  if (lane < p.n_slots - 1) dst[2 + lane] = p.expert;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -197,11 +212,11 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // Persistent: grid = resident workgroups, WA waves each.  The tasks are
 // (expert slot, group of P intermediate rows); wave w of the grid takes tasks
 // w, w + NW, w + 2 NW, ... (NW = all waves).  A wave streams its tasks as one
-// sequence of (task, 1024-wide chunk of the hidden dim) units; with PF = 1 the
-// loads of the next unit are issued before the current one is computed, so a
-// wave keeps 2P rows of weights in flight while it decodes and multiplies.
+// sequence of (task, 1024-wide chunk of the hidden dim) units and keeps the
+// loads of the next DUCKMOE_GU_DEPTH - 1 units in flight while it decodes and
+// multiplies the current one.
 // The TG tokens t0 .. t0+TG-1 of the call are handled; their activations sit in
-// LDS for the whole kernel.  Dynamic LDS: max(TG * H, 2 * kMaxWords) floats.
+// LDS for the whole kernel.  Dynamic LDS: TG rows of H floats, padded to whole chunks.
 template <int P>
 struct GuTile {
   uint4 d[2][P];
@@ -218,11 +233,9 @@ struct GuUnit {              // where one (task, chunk) unit reads from
 };
 
 template <int P>
-__device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, const PlanLds &plan, int task,
-                                          int c) {
+__device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, int e, int task, int c) {
   const int NB = a.I / P;
   const int slot = task / NB;
-  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
   const uint32_t mat = (uint32_t)a.I * (uint32_t)a.H;
   GuUnit u;
   u.rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
@@ -237,7 +250,7 @@ __device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, const PlanLds &pla
 
 // The unit after u in a wave's sequence: next chunk, or chunk 0 of task + NW.
 template <int P>
-__device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const PlanLds &plan,
+__device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const WavePlan &plan,
                                           const GuUnit &u, int nc, int NW, int ntask) {
   if (u.c + 1 < nc) {
     GuUnit n = u;
@@ -245,7 +258,8 @@ __device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const PlanLds &pla
     n.kc = u.kc + kChunk;
     return n;
   }
-  if (u.task + NW < ntask) return gu_unit<P>(a, plan, u.task + NW, 0);
+  const int t = u.task + NW;
+  if (t < ntask) return gu_unit<P>(a, plan_expert(plan, t / (a.I / P)), t, 0);
   GuUnit n = u;
   n.task = ntask;  // past the end
   return n;
@@ -294,7 +308,7 @@ __device__ __forceinline__ void gu_consume(const GuTile<P> &b, const float4 *xs4
 }
 
 template <int TG, int P>
-__device__ __forceinline__ void gu_finish(const LayerArgs &a, const PlanLds &plan, int slot,
+__device__ __forceinline__ void gu_finish(const LayerArgs &a, const WavePlan &plan, int slot,
                                           uint32_t row0, int t0, int lane,
                                           float (&acc)[2][P][TG][2]) {
 #pragma unroll
@@ -304,8 +318,8 @@ __device__ __forceinline__ void gu_finish(const LayerArgs &a, const PlanLds &pla
       const float gsum = wave_sum(acc[0][p][t][0] + acc[0][p][t][1]);
       const float vsum = wave_sum(acc[1][p][t][0] + acc[1][p][t][1]);
       acc[0][p][t][0] = acc[0][p][t][1] = acc[1][p][t][0] = acc[1][p][t][1] = 0.0f;
+      const float wt = plan_weight(plan, a, slot, t0 + t);
       if (lane == 0) {
-        const float wt = plan.w[slot][t0 + t];
         const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gsum) * vsum);
         a.hbuf[((size_t)slot * a.T + t0 + t) * a.I + row0 + p] = hv;
       }
@@ -314,7 +328,6 @@ __device__ __forceinline__ void gu_finish(const LayerArgs &a, const PlanLds &pla
 
 template <int TG, int P, int WA>
 __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const int t0) {
-  __shared__ PlanLds plan;
   extern __shared__ float4 xs4[];  // [TG][nc * 256]: rows padded with zeros to whole chunks
   constexpr int NT = WA * 64;
   constexpr int XR = 8;  // float4 of x per thread loaded before the plan
@@ -322,52 +335,57 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
   const int nc = (H + kChunk - 1) / kChunk;
   const int Hp4 = nc * (kChunk / 4);
   const int n4 = TG * Hp4;
-  const float4 *xg = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
-
-  // ids first, then x: the x loads' latency overlaps the plan
-  const PlanIn pin = plan_load(a);
-  float4 xr[XR];
-#pragma unroll
-  for (int j = 0; j < XR; ++j) {
-    const int q = threadIdx.x + j * NT;
-    const int t = q / Hp4, k4 = q - t * Hp4;
-    xr[j] = (q < n4 && k4 < H4) ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  build_plan(plan, a, pin, reinterpret_cast<uint32_t *>(xs4),
-             reinterpret_cast<int *>(xs4) + kMaxWords);  // ends with a barrier
-  if (blockIdx.x == 0 && t0 == 0) {
-    int32_t *wsplan = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(a.hdr) + kPlanOff);
-    if (threadIdx.x == 0) {
-      a.hdr->status = plan.status;
-      a.hdr->n_slots = plan.n_slots;
-      wsplan[0] = plan.n_slots;
-    }
-    for (int i = threadIdx.x; i < plan.n_slots; i += NT) wsplan[1 + i] = plan.expert[i];
-  }
-
+  const int NB = a.I / P;  // tasks per slot
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NW = gridDim.x * WA;
+#if DUCKMOE_GU_MAP
+  const int gw = wave * gridDim.x + blockIdx.x;
+#else
   const int gw = blockIdx.x * WA + wave;
-  const int ntask = plan.n_slots * (a.I / P);
+#endif
 
+  // A wave whose first task lies in slot 0 (known without the ids) issues its
+  // first weight loads at once; then the ids; then x.
   GuTile<P> b0, b1;
-  GuUnit u0, u1;
-  u0.task = ntask;
-  if (gw < ntask) {
-    u0 = gu_unit<P>(a, plan, gw, 0);
+  GuUnit u0;
+  const bool early = gw < NB;
+  if (early) {
+    u0 = gu_unit<P>(a, slot0_expert(a), gw, 0);
     gu_issue(b0, u0, a, lane);
   }
+  const PlanIn pin = plan_load(a);
+  // x rows t0 .. t0 + TG - 1; unconditional buffer loads, zero past each row's end
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)t0 * H, (uint32_t)(TG * H) * 4u);
+  auto x_off = [&](int q) -> uint32_t {
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    return (q < n4 && k4 < H4) ? (uint32_t)(t * H4 + k4) * 16u : kOutOfRange;
+  };
+  float4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) xr[j] = buf_loadf4(rx, x_off(threadIdx.x + j * NT));
+
+  const WavePlan plan = wave_plan(a, pin);
+  if (blockIdx.x == 0 && wave == 0 && t0 == 0) plan_store(plan, a);
+  const int ntask = plan.n_slots * NB;
+  if (!early) {
+    if (gw < ntask) {
+      u0 = gu_unit<P>(a, plan_expert(plan, gw / NB), gw, 0);
+      gu_issue(b0, u0, a, lane);
+    } else {
+      u0 = gu_unit<P>(a, plan.e0, 0, 0);
+      u0.task = ntask;  // no work: past the end
+    }
+  }
+
   // activations into LDS (the first XR float4 per thread are already loaded)
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
     const int q = threadIdx.x + j * NT;
     if (q < n4) xs4[q] = xr[j];
   }
-  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) {
-    const int t = q / Hp4, k4 = q - t * Hp4;
-    xs4[q] = k4 < H4 ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+#pragma unroll 4
+  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) xs4[q] = buf_loadf4(rx, x_off(q));
   __syncthreads();
 
   float acc[2][P][TG][2];
@@ -378,21 +396,45 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
 #pragma unroll
       for (int t = 0; t < TG; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
 
-  // Two units per trip so that the register buffers keep static names.
+  // The next DEPTH - 1 units' loads are in flight while a unit is computed.
+  // DEPTH units per trip so that the register buffers keep static names.
+  GuUnit u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+#if DUCKMOE_GU_DEPTH == 3
+  if (u1.task < ntask) gu_issue(b1, u1, a, lane);
+  GuTile<P> b2;
+  GuUnit u2;
   while (u0.task < ntask) {
-    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
-    if (DUCKMOE_GU_PREFETCH && u1.task < ntask) gu_issue(b1, u1, a, lane);
+    u2 = gu_next<P>(a, plan, u1, nc, NW, ntask);
+    if (u2.task < ntask) gu_issue(b2, u2, a, lane);
     gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc);
     if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
     if (u1.task >= ntask) break;
-    if (!DUCKMOE_GU_PREFETCH) gu_issue(b1, u1, a, lane);
 
-    u0 = gu_next<P>(a, plan, u1, nc, NW, ntask);
-    if (DUCKMOE_GU_PREFETCH && u0.task < ntask) gu_issue(b0, u0, a, lane);
+    u0 = gu_next<P>(a, plan, u2, nc, NW, ntask);
+    if (u0.task < ntask) gu_issue(b0, u0, a, lane);
     gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc);
     if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
-    if (!DUCKMOE_GU_PREFETCH && u0.task < ntask) gu_issue(b0, u0, a, lane);
+    if (u2.task >= ntask) break;
+
+    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+    if (u1.task < ntask) gu_issue(b1, u1, a, lane);
+    gu_consume<TG, P>(b2, xs4, Hp4, u2.kc, lane, acc);
+    if (u2.c == nc - 1) gu_finish<TG, P>(a, plan, u2.slot, u2.row0, t0, lane, acc);
   }
+#else
+  while (u0.task < ntask) {
+    if (u1.task < ntask) gu_issue(b1, u1, a, lane);
+    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc);
+    if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
+    if (u1.task >= ntask) break;
+
+    u0 = gu_next<P>(a, plan, u1, nc, NW, ntask);
+    if (u0.task < ntask) gu_issue(b0, u0, a, lane);
+    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc);
+    if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
+    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+  }
+#endif
 }
 
 // ------------------------------------------------------------------ down ----
@@ -405,7 +447,7 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
 // wave reduces its lanes in groups as wide as a shard slice, the groups' sums
 // meet in LDS, and the waves' sums are added in a fixed order: each output
 // element is written once, no atomics, bit-reproducible.
-// Dynamic LDS: max(WB * R * T * 16, 2 * kMaxWords) floats.
+// Dynamic LDS: WB * R * T * 16 floats.
 template <int G>
 __device__ __forceinline__ void store_groups(float v, float *dst, int lane) {
   v = group_sum<G>(v);
@@ -420,12 +462,11 @@ struct DnTile {
 };
 
 template <int T, int R>
-__device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, const int32_t *plan,
+__device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, int e,
                                          __amdgpu_buffer_rsrc_t rh, int slot, int row0,
                                          uint32_t k, bool kv) {
   const uint32_t H = a.H, I = a.I;
   const uint32_t mat = H * I;
-  const int e = __builtin_amdgcn_readfirstlane(plan[1 + slot]);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
 #pragma unroll
@@ -469,6 +510,11 @@ __device__ __forceinline__ void dn_consume(const DnTile<T, R> &b, float (&acc)[R
 // The n_it items (slots s0, s0 + per_c, ...) of one block for one wave.  The
 // first item is already in flight in b0; items alternate between b0 and b1,
 // the next one always issued before the current one is computed.
+// expert of slot s in the plan the gate/up launch left in the workspace
+__device__ __forceinline__ int plan_at(const int32_t *plan, int s) {
+  return __builtin_amdgcn_readfirstlane(plan[1 + s]);
+}
+
 template <int T, int R>
 __device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, const LayerArgs &a,
                                          const int32_t *plan, __amdgpu_buffer_rsrc_t rh,
@@ -476,10 +522,12 @@ __device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, con
                                          bool kv, float (&acc)[R][T][2]) {
   for (int i = 0; i < n_it; i += 2) {
     const int slot = s0 + i * per_c;
-    if (i + 1 < n_it) dn_issue<T, R>(b1, a, plan, rh, slot + per_c, blk * R, k, kv);
+    if (i + 1 < n_it)
+      dn_issue<T, R>(b1, a, plan_at(plan, slot + per_c), rh, slot + per_c, blk * R, k, kv);
     dn_consume<T, R>(b0, acc);
     if (i + 1 >= n_it) break;
-    if (i + 2 < n_it) dn_issue<T, R>(b0, a, plan, rh, slot + 2 * per_c, blk * R, k, kv);
+    if (i + 2 < n_it)
+      dn_issue<T, R>(b0, a, plan_at(plan, slot + 2 * per_c), rh, slot + 2 * per_c, blk * R, k, kv);
     dn_consume<T, R>(b1, acc);
   }
 }
@@ -495,21 +543,28 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nc = (I + kChunk - 1) / kChunk;
   const int per_c = WB / nc;  // waves per chunk
-  const int S = __builtin_amdgcn_readfirstlane(plan[0]);
   const int nblk = (H + R - 1) / R;
   const int c = wave % nc;
   const uint32_t k = (uint32_t)c * kChunk + lane * 16;
   const bool kv = k < (uint32_t)I;
   const int s0 = wave / nc;  // first slot of this wave in every block
-  // items per block for this wave (0 for waves beyond nc * per_c)
-  const int n_it = (wave < nc * per_c && s0 < S) ? (S - s0 + per_c - 1) / per_c : 0;
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, (uint32_t)(S * a.T * I) * 4u);
+  const bool active = wave < nc * per_c;
+  // h' of every slot the workspace can hold; slots >= n_slots are never read
+  const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, (uint32_t)(max_slots * a.T * I) * 4u);
   const int ns = a.n_shards;
   const int width = I / ns;
 
+  // A wave whose first item is slot 0 (its expert is known without the plan)
+  // issues it before the plan arrives.
   DnTile<T, R> b0, b1;
-  if (n_it > 0 && (int)blockIdx.x < nblk)
-    dn_issue<T, R>(b0, a, plan, rh, s0, blockIdx.x * R, k, kv);
+  const bool first_now = active && s0 == 0 && (int)blockIdx.x < nblk;
+  if (first_now) dn_issue<T, R>(b0, a, slot0_expert(a), rh, 0, blockIdx.x * R, k, kv);
+  const int S = __builtin_amdgcn_readfirstlane(plan[0]);
+  // items per block for this wave (0 for waves beyond nc * per_c)
+  const int n_it = (active && s0 < S) ? (S - s0 + per_c - 1) / per_c : 0;
+  if (!first_now && n_it > 0 && (int)blockIdx.x < nblk)
+    dn_issue<T, R>(b0, a, plan_at(plan, s0), rh, s0, blockIdx.x * R, k, kv);
 
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     float acc[R][T][2];
@@ -522,7 +577,7 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
       dn_block<T, R>(b0, b1, a, plan, rh, blk, s0, per_c, n_it, k, kv, acc);
       // the next block's first item loads while this block is reduced
       if (blk + (int)gridDim.x < nblk)
-        dn_issue<T, R>(b0, a, plan, rh, s0, (blk + gridDim.x) * R, k, kv);
+        dn_issue<T, R>(b0, a, plan_at(plan, s0), rh, s0, (blk + gridDim.x) * R, k, kv);
     }
 
     // lane groups of G lanes -> 64/G partial sums per (wave, row, token)
@@ -568,484 +623,6 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
     }
     __syncthreads();  // red is rewritten by the next block
   }
-}
-
-// ----------------------------------------------------------------- fused ----
-// One launch for the whole layer (T <= 2).  The intermediate dimension is cut
-// into n_xcd slices of Ix = I / n_xcd rows, one per XCD of the chip (logical
-// XCD of workgroup b: b % n_xcd, which is where the hardware places it); each
-// XCD is a tensor-parallel shard in the pages' sense:
-//   A. its workgroups stream the gate/up rows of their slice for every plan
-//      slot (balanced contiguous ranges of (row pair, 1024-chunk) units per
-//      wave; a pair split between two waves is completed through LDS) and
-//      write h' with write-through stores;
-//   B. once every workgroup of the XCD has finished A (one counter per XCD),
-//      each workgroup stages the XCD's h' slice in LDS and streams the down
-//      matrices restricted to the slice's columns for a block of output rows,
-//      all slots summed;
-//   C. the XCD partials of a row block meet in the workspace; the XCD that
-//      arrives last (a counter per row block) adds the n_xcd partials in XCD
-//      order and writes the output.  In shard mode with one or more shards per
-//      XCD, the shard sums are written directly instead.
-// Producer/consumer traffic between workgroups uses write-through stores,
-// device-coherent atomics and cache-bypassing loads, never a device-scope
-// fence (those serialise across the chip).  Waits are bounded (kFuSpin); a
-// timeout sets DUCKMOE_STATUS_TIMEOUT.  Every counter is back at zero when the
-// launch ends, so a zero-filled workspace stays valid from call to call.
-#ifndef DUCKMOE_FU_WAVES
-#define DUCKMOE_FU_WAVES 8
-#endif
-constexpr int kFuSpin = 1 << 22;
-constexpr size_t kFuDoneOff = 256;     // uint32 doneA[x] at 256 + 128 x
-constexpr size_t kFuPassOff = 1280;    // uint32 passed[x] at 1280 + 128 x
-constexpr size_t kFuCntOff = 8192;     // uint32 cnt[r] at 8192 + 64 r
-constexpr int kFuMaxXcd = 8;
-constexpr int kFuMaxBlocks = 128;      // row blocks (workgroups per XCD)
-
-struct FuArgs {
-  uint8_t *hdr;   // workspace header
-  float *Y;       // [n_xcd][T][H] XCD partials
-  int n_xcd;
-  int G;          // lanes per reduction group in B (lane groups of one shard, or of one row)
-};
-
-// Phase timestamps (s_memrealtime, 100 MHz) per workgroup, for profiling builds
-// only (-DDUCKMOE_FU_TRACE): 8 x u64 per workgroup after the workspace's end.
-#ifdef DUCKMOE_FU_TRACE
-#define FU_MARK(f, i)                                                                   \
-  do {                                                                                \
-    if (threadIdx.x == 0)                                                             \
-      reinterpret_cast<unsigned long long *>((f).Y + (size_t)kFuMaxXcd * a.T * a.H)[  \
-          blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime();                   \
-  } while (0)
-#else
-#define FU_MARK(f, i) do { } while (0)
-#endif
-
-__device__ __forceinline__ uint32_t *fu_done(const FuArgs &f, int x) {
-  return reinterpret_cast<uint32_t *>(f.hdr + kFuDoneOff + 128 * x);
-}
-__device__ __forceinline__ uint32_t *fu_pass(const FuArgs &f, int x) {
-  return reinterpret_cast<uint32_t *>(f.hdr + kFuPassOff + 128 * x);
-}
-__device__ __forceinline__ uint32_t *fu_cnt(const FuArgs &f, int r) {
-  return reinterpret_cast<uint32_t *>(f.hdr + kFuCntOff + 64 * r);
-}
-__device__ __forceinline__ void st_through(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ float ld_through(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ uint32_t ld_ctr(uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t add_ctr(uint32_t *p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_ctr(uint32_t *p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// h' of one (slot, row) from the reduced gate/up sums
-__device__ __forceinline__ float swiglu_w(float wt, float g, float v) {
-  return (wt == 0.0f) ? 0.0f : wt * (silu(g) * v);
-}
-
-// B unit: M row groups of RPU rows (one slot's down matrix, the XCD slice's
-// columns).  Lane l covers rows q*M*RPU + m*RPU + l / LR (m < M) and the 16
-// columns at (l % LR) * 16 of the slice.
-#ifndef DUCKMOE_FU_BROWS
-#define DUCKMOE_FU_BROWS 4  // M: row groups per lane per B unit
-#endif
-template <int M>
-struct FbTile {
-  uint4 d[M];
-  uint32_t s[M];
-};
-
-template <int M>
-__device__ __forceinline__ void fb_issue(FbTile<M> &b, const LayerArgs &a,
-                                         __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rs,
-                                         int q, int RPU, int LR, uint32_t kx, int lane) {
-  const uint32_t H = a.H, I = a.I;
-  const uint32_t k = kx + (uint32_t)(lane % LR) * 16;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t row = (uint32_t)((q * M + m) * RPU + lane / LR);
-    const bool ok = row < H;
-    b.d[m] = buf_load16(rb, ok ? row * I + k : kOutOfRange);
-    b.s[m] = buf_load2(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
-  }
-}
-
-template <int T, int M>
-__device__ __forceinline__ void fb_consume(const FbTile<M> &b, const float *hs, int Ix, int slot,
-                                           int LR, int lane, float (&acc)[M][T][2]) {
-  float xv[T][16];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const float4 *src =
-        reinterpret_cast<const float4 *>(hs + (slot * T + t) * Ix + (lane % LR) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = src[j];
-      xv[t][4 * j] = v.x; xv[t][4 * j + 1] = v.y; xv[t][4 * j + 2] = v.z; xv[t][4 * j + 3] = v.w;
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    h2_t h[8];
-    fp9_decode16(b.d[m], b.s[m], h);
-#pragma unroll
-    for (int t = 0; t < T; ++t) fma16(h, xv[t], acc[m][t][0], acc[m][t][1]);
-  }
-}
-
-__device__ __forceinline__ float fb_reduce(float v, int G) {
-  switch (G) {
-    case 4: return group_sum<4>(v);
-    case 8: return group_sum<8>(v);
-    case 16: return group_sum<16>(v);
-    case 32: return group_sum<32>(v);
-    default: return group_sum<64>(v);
-  }
-}
-
-// A cursor over (row pair, chunk) units; pr = pair index within the XCD's list
-// (slot-major), ris = row of the pair inside its slot's slice.
-struct FaCur {
-  int u, pr, c, slot, ris;
-};
-
-__device__ __forceinline__ void fa_rsrc(const LayerArgs &a, const PlanLds &plan, int slot,
-                                        __amdgpu_buffer_rsrc_t &rb, __amdgpu_buffer_rsrc_t &rs) {
-  const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
-  const uint32_t mat = (uint32_t)a.I * (uint32_t)a.H;
-  rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
-  rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
-}
-
-template <int T, int WA>
-__global__ __launch_bounds__(WA * 64) void k_fused(const LayerArgs a, const FuArgs f) {
-  constexpr int M = DUCKMOE_FU_BROWS;
-  __shared__ PlanLds plan;
-  __shared__ int meta[WA][2];            // pair / row-block index of each wave's split ends
-  __shared__ float pa[WA][2][T][2];      // A split partials (g, v)
-  __shared__ float pb[WA][2][M][T][16];  // B split partials (64 / G groups per row group)
-  __shared__ uint32_t bcast;
-  extern __shared__ float4 lds4[];       // xs [T][Hp] | hs [S][T][Ix]
-  constexpr int NT = WA * 64;
-  constexpr int XR = 8;
-  const int H = a.H, I = a.I, H4 = a.H / 4;
-  const int nc = (H + kChunk - 1) / kChunk;
-  const int Hp4 = nc * (kChunk / 4);
-  const int n4 = T * Hp4;
-  const float4 *xg = reinterpret_cast<const float4 *>(a.x);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  FU_MARK(f, 0);
-
-  // ---- prologue: ids, then x loads overlapping the plan; x into LDS
-  const PlanIn pin = plan_load(a);
-  float4 xr[XR];
-#pragma unroll
-  for (int j = 0; j < XR; ++j) {
-    const int q = threadIdx.x + j * NT;
-    const int t = q / Hp4, k4 = q - t * Hp4;
-    xr[j] = (q < n4 && k4 < H4) ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  build_plan(plan, a, pin, reinterpret_cast<uint32_t *>(lds4),
-             reinterpret_cast<int *>(lds4) + kMaxWords);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.hdr->status = plan.status;
-    a.hdr->n_slots = plan.n_slots;
-  }
-#pragma unroll
-  for (int j = 0; j < XR; ++j) {
-    const int q = threadIdx.x + j * NT;
-    if (q < n4) lds4[q] = xr[j];
-  }
-  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) {
-    const int t = q / Hp4, k4 = q - t * Hp4;
-    lds4[q] = k4 < H4 ? xg[t * H4 + k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (threadIdx.x < 2 * WA) (&meta[0][0])[threadIdx.x] = -1;
-  __syncthreads();
-  FU_MARK(f, 1);
-
-  const int S = plan.n_slots;
-  const int nx = f.n_xcd;
-  const int xcd = blockIdx.x % nx;
-  const int r = blockIdx.x / nx;
-  const int Gx = gridDim.x / nx;
-  const int Ix = I / nx;
-  const uint32_t kx = (uint32_t)xcd * Ix;
-  float *hs = reinterpret_cast<float *>(lds4 + n4);
-
-  // ---- A: gate/up pairs of this XCD's slice
-  {
-    const int PT = S * Ix;
-    const int p0 = (int)((long)r * PT / Gx), p1 = (int)((long)(r + 1) * PT / Gx);
-    const int U = (p1 - p0) * nc;
-    const int u0 = (int)((long)wave * U / WA), u1 = (int)((long)(wave + 1) * U / WA);
-    float acc[2][1][T][2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[g][0][t][0] = acc[g][0][t][1] = 0.0f;
-    // at the last unit of a pair, or of the range: reduce, then finish or park
-    auto pair_end = [&](const FaCur &cu) {
-      const bool whole_start = cu.u - cu.c >= u0;  // the pair's chunk 0 is in range
-      const bool done = cu.c == nc - 1;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float gs = wave_sum(acc[0][0][t][0] + acc[0][0][t][1]);
-        const float vs = wave_sum(acc[1][0][t][0] + acc[1][0][t][1]);
-        acc[0][0][t][0] = acc[0][0][t][1] = acc[1][0][t][0] = acc[1][0][t][1] = 0.0f;
-        if (lane == 0) {
-          if (whole_start && done) {
-            st_through(a.hbuf + ((size_t)cu.slot * T + t) * I + kx + cu.ris,
-                       swiglu_w(plan.w[cu.slot][t], gs, vs));
-          } else {
-            pa[wave][whole_start ? 1 : 0][t][0] = gs;
-            pa[wave][whole_start ? 1 : 0][t][1] = vs;
-          }
-        }
-      }
-      if (!(whole_start && done) && lane == 0) meta[wave][whole_start ? 1 : 0] = cu.pr;
-    };
-    if (u0 < u1) {
-      FaCur cur;
-      cur.u = u0;
-      cur.pr = p0 + u0 / nc;
-      cur.c = u0 - (cur.pr - p0) * nc;
-      cur.slot = cur.pr / Ix;
-      cur.ris = cur.pr - cur.slot * Ix;
-      __amdgpu_buffer_rsrc_t rb, rs;
-      fa_rsrc(a, plan, cur.slot, rb, rs);
-      auto unit = [&](const FaCur &cu) {
-        GuUnit un;
-        un.rb = rb;
-        un.rs = rs;
-        un.row0 = kx + (uint32_t)cu.ris;
-        un.kc = (uint32_t)cu.c * kChunk;
-        return un;
-      };
-      auto advance = [&](FaCur &cu) {
-        ++cu.u;
-        if (++cu.c == nc) {
-          cu.c = 0;
-          ++cu.pr;
-          if (++cu.ris == Ix) {
-            cu.ris = 0;
-            ++cu.slot;
-            if (cu.u < u1) fa_rsrc(a, plan, cu.slot, rb, rs);
-          }
-        }
-      };
-      GuTile<1> b0, b1;
-      FaCur c0 = cur, c1;
-      gu_issue(b0, unit(c0), a, lane);
-      while (true) {
-        c1 = c0;
-        advance(c1);
-        if (c1.u < u1) gu_issue(b1, unit(c1), a, lane);
-        gu_consume<T, 1>(b0, lds4, Hp4, (uint32_t)c0.c * kChunk, lane, acc);
-        if (c0.c == nc - 1 || c0.u + 1 == u1) pair_end(c0);
-        if (c1.u >= u1) break;
-        c0 = c1;
-        advance(c0);
-        if (c0.u < u1) gu_issue(b0, unit(c0), a, lane);
-        gu_consume<T, 1>(b1, lds4, Hp4, (uint32_t)c1.c * kChunk, lane, acc);
-        if (c1.c == nc - 1 || c1.u + 1 == u1) pair_end(c1);
-        if (c0.u >= u1) break;
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  FU_MARK(f, 2);
-  // pairs split between waves: sum the parts in wave order, then finish
-  if (threadIdx.x < 2 * WA) {
-    const int w = threadIdx.x >> 1, side = threadIdx.x & 1;
-    const int pr = meta[w][side];
-    bool first = pr >= 0;
-    for (int w2 = 0; w2 <= w && first; ++w2)
-      for (int s2 = 0; s2 < 2; ++s2)
-        if ((w2 < w || s2 < side) && meta[w2][s2] == pr) first = false;
-    if (first) {
-      const int slot = pr / Ix;
-      for (int t = 0; t < T; ++t) {
-        float gs = 0.0f, vs = 0.0f;
-        for (int w2 = 0; w2 < WA; ++w2)
-          for (int s2 = 0; s2 < 2; ++s2)
-            if (meta[w2][s2] == pr) { gs += pa[w2][s2][t][0]; vs += pa[w2][s2][t][1]; }
-        st_through(a.hbuf + ((size_t)slot * T + t) * I + kx + (pr - slot * Ix),
-                   swiglu_w(plan.w[slot][t], gs, vs));
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x < 2 * WA) (&meta[0][0])[threadIdx.x] = -1;
-
-  // ---- B setup: this workgroup's row blocks; first unit in flight during the wait
-  const int LR = Ix / 16;          // lanes per row
-  const int RPU = 64 / LR;         // rows per row group
-  const int nq = (H + M * RPU - 1) / (M * RPU);
-  const int q0 = (int)((long)r * nq / Gx), q1 = (int)((long)(r + 1) * nq / Gx);
-  const int UB = (q1 - q0) * S;
-  const int ub0 = (int)((long)wave * UB / WA), ub1 = (int)((long)(wave + 1) * UB / WA);
-  const uint32_t dmat = (uint32_t)H * (uint32_t)I;
-  auto drsrc = [&](int slot, __amdgpu_buffer_rsrc_t &rb, __amdgpu_buffer_rsrc_t &rs) {
-    const int e = __builtin_amdgcn_readfirstlane(plan.expert[slot]);
-    rb = make_rsrc(a.dn_body + (size_t)e * dmat, dmat);
-    rs = make_rsrc(a.dn_sign + (size_t)e * (dmat / 8), dmat / 8);
-  };
-  FbTile<M> t0, t1;
-  int bq = 0, bs = 0;  // B cursor: row block, slot
-  if (ub0 < ub1) {
-    bq = q0 + ub0 / S;
-    bs = ub0 - (bq - q0) * S;
-    __amdgpu_buffer_rsrc_t rb, rs;
-    drsrc(bs, rb, rs);
-    fb_issue<M>(t0, a, rb, rs, bq, RPU, LR, kx, lane);
-  }
-
-  // ---- wait for the XCD's A phase; stage its h' slice
-  if (threadIdx.x == 0) {
-    add_ctr(fu_done(f, xcd), 1u);
-    int it = 0;
-    while (ld_ctr(fu_done(f, xcd)) < (uint32_t)Gx && it < kFuSpin) {
-      __builtin_amdgcn_s_sleep(2);
-      ++it;
-    }
-    if (it >= kFuSpin) atomicOr(&a.hdr->status, DUCKMOE_STATUS_TIMEOUT);
-  }
-  __syncthreads();
-  FU_MARK(f, 3);
-  if (threadIdx.x == 0) {
-    if (add_ctr(fu_pass(f, xcd), 1u) == (uint32_t)Gx - 1) {  // everyone is past the wait
-      st_ctr(fu_done(f, xcd), 0u);
-      st_ctr(fu_pass(f, xcd), 0u);
-    }
-  }
-  for (int q = threadIdx.x; q < S * T * Ix; q += NT) {
-    const int st = q / Ix, i = q - st * Ix;  // st = slot * T + t
-    hs[q] = ld_through(a.hbuf + (size_t)st * I + kx + i);
-  }
-  __syncthreads();
-  FU_MARK(f, 4);
-
-  // ---- B: down rows x slice columns, all slots; units (row block q, slot s)
-  const int G = f.G;               // lanes per reduction group
-  const int ns = a.n_shards;
-  {
-    float acc[M][T][2];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[m][t][0] = acc[m][t][1] = 0.0f;
-    auto emit = [&](int row, int t, int lanepos, float v) {
-      if (row >= H) return;
-      if (ns == 1) {
-        st_through(f.Y + ((size_t)xcd * T + t) * H + row, v);
-      } else {
-        const int shard = (int)((kx + (lanepos % LR) / G * G * 16) / (uint32_t)(I / ns));
-        a.out[((size_t)shard * T + t) * H + row] = v;
-      }
-    };
-    // after the last slot of a row block, or at the end of the range
-    auto block_end = [&](int u, int q, int sl) {
-      const bool whole_start = u - sl >= ub0;
-      const bool done = sl == S - 1;
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const float v = fb_reduce(acc[m][t][0] + acc[m][t][1], G);
-          acc[m][t][0] = acc[m][t][1] = 0.0f;
-          if ((lane & (G - 1)) == G - 1) {
-            if (whole_start && done)
-              emit((q * M + m) * RPU + lane / LR, t, lane, v);
-            else
-              pb[wave][whole_start ? 1 : 0][m][t][lane / G] = v;
-          }
-        }
-      if (!(whole_start && done) && lane == 0) meta[wave][whole_start ? 1 : 0] = q;
-    };
-    if (ub0 < ub1) {
-      __amdgpu_buffer_rsrc_t rb, rs;
-      int u = ub0, q = bq, sl = bs;
-      while (true) {
-        // next unit's cursor
-        int q1n = q, s1n = sl + 1;
-        if (s1n == S) { s1n = 0; ++q1n; }
-        if (u + 1 < ub1) { drsrc(s1n, rb, rs); fb_issue<M>(t1, a, rb, rs, q1n, RPU, LR, kx, lane); }
-        fb_consume<T, M>(t0, hs, Ix, sl, LR, lane, acc);
-        if (sl == S - 1 || u + 1 == ub1) block_end(u, q, sl);
-        if (++u >= ub1) break;
-        q = q1n; sl = s1n;
-        int q2n = q, s2n = sl + 1;
-        if (s2n == S) { s2n = 0; ++q2n; }
-        if (u + 1 < ub1) { drsrc(s2n, rb, rs); fb_issue<M>(t0, a, rb, rs, q2n, RPU, LR, kx, lane); }
-        fb_consume<T, M>(t1, hs, Ix, sl, LR, lane, acc);
-        if (sl == S - 1 || u + 1 == ub1) block_end(u, q, sl);
-        if (++u >= ub1) break;
-        q = q2n; sl = s2n;
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  FU_MARK(f, 5);
-  // row blocks split between waves: sum the parts in wave order
-  for (int e = threadIdx.x; e < 2 * WA * 64; e += NT) {
-    const int ws = e / 64, ln = e % 64;  // (wave, side) entry, lane position
-    const int w = ws >> 1, side = ws & 1;
-    const int q = meta[w][side];
-    if (q < 0 || (ln & (G - 1)) != G - 1) continue;
-    bool first = true;
-    for (int w2 = 0; w2 <= w && first; ++w2)
-      for (int s2 = 0; s2 < 2; ++s2)
-        if ((w2 < w || s2 < side) && meta[w2][s2] == q) first = false;
-    if (!first) continue;
-    for (int m = 0; m < M; ++m) {
-      const int row = (q * M + m) * RPU + ln / LR;
-      if (row >= H) continue;
-      for (int t = 0; t < T; ++t) {
-        float v = 0.0f;
-        for (int w2 = 0; w2 < WA; ++w2)
-          for (int s2 = 0; s2 < 2; ++s2)
-            if (meta[w2][s2] == q) v += pb[w2][s2][m][t][ln / G];
-        if (ns == 1) {
-          st_through(f.Y + ((size_t)xcd * T + t) * H + row, v);
-        } else {
-          const int shard = (int)((kx + (ln % LR) / G * G * 16) / (uint32_t)(I / ns));
-          a.out[((size_t)shard * T + t) * H + row] = v;
-        }
-      }
-    }
-  }
-  if (ns != 1) return;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // ---- C: the last XCD to finish this row range adds the partials in XCD order
-  FU_MARK(f, 6);
-  if (threadIdx.x == 0) bcast = add_ctr(fu_cnt(f, r), 1u);
-  __syncthreads();
-  if (bcast != (uint32_t)nx - 1) return;
-  const int row_lo = q0 * M * RPU, row_hi = min(q1 * M * RPU, H);
-  for (int q = threadIdx.x; q < (row_hi - row_lo) * T; q += NT) {
-    const int t = q / (row_hi - row_lo), row = row_lo + q % (row_hi - row_lo);
-    float v = 0.0f;
-    for (int x2 = 0; x2 < nx; ++x2) v += ld_through(f.Y + ((size_t)x2 * T + t) * H + row);
-    a.out[(size_t)t * H + row] = v;
-  }
-  if (threadIdx.x == 0) st_ctr(fu_cnt(f, r), 0u);
-  FU_MARK(f, 7);
 }
 
 // ------------------------------------------------------ building blocks ----
@@ -1109,11 +686,13 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t *__restrict__ body,
 }
 
 __global__ __launch_bounds__(64) void k_plan(const LayerArgs a, int32_t *uniq, int32_t *n_slots) {
-  __shared__ PlanLds plan;
-  __shared__ uint32_t scratch[2 * kMaxWords];
-  build_plan(plan, a, plan_load(a), scratch, reinterpret_cast<int *>(scratch) + kMaxWords);
-  for (int s = threadIdx.x; s < plan.n_slots; s += blockDim.x) uniq[s] = plan.expert[s];
-  if (threadIdx.x == 0) *n_slots = plan.n_slots;
+  const WavePlan p = wave_plan(a, plan_load(a));
+  const int lane = threadIdx.x;
+  if (lane == 0) {
+    uniq[0] = p.e0;
+    *n_slots = p.n_slots;
+  }
+  if (lane < p.n_slots - 1) uniq[1 + lane] = p.expert;
 }
 
 // ------------------------------------------------------------ host side ----
@@ -1166,10 +745,9 @@ size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
   return hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
 }
 
-// header | h' [slots][T][I] | XCD partials [kFuMaxXcd][T][H] (fused path)
+// header | h' [slots][T][I]
 size_t ws_need(const duckmoe_layer *L, int T, bool single) {
-  return kHdrBytes + hbuf_bytes(L, T, single) +
-         (size_t)kFuMaxXcd * T * L->hidden * sizeof(float);
+  return kHdrBytes + hbuf_bytes(L, T, single);
 }
 
 // Launch shape of the down kernel (compile-time; defaults measured on MI355X).
@@ -1212,7 +790,7 @@ hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
   constexpr int P = DUCKMOE_GU_PAIRS, WA = DUCKMOE_GU_WAVES;
   const auto kern = k_gate_up<TG, P, WA>;
   const size_t hp = (size_t)((a.H + kChunk - 1) / kChunk) * kChunk;
-  const size_t lds = std::max((size_t)TG * hp * sizeof(float), (size_t)2 * kMaxWords * 4);
+  const size_t lds = (size_t)TG * hp * sizeof(float);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -1272,69 +850,6 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
   }
 }
 
-#ifndef DUCKMOE_FU_WAVES_PER_CU
-#define DUCKMOE_FU_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
-#endif
-#ifndef DUCKMOE_FU_COOPERATIVE
-#define DUCKMOE_FU_COOPERATIVE 0    // 1: cooperative launch (co-residency guaranteed, ~17 us slower)
-#endif
-#ifndef DUCKMOE_FUSED
-#define DUCKMOE_FUSED 0             // 1: single-launch layer for T <= 2 (slower than two launches
-                                    //    as measured on MI355X; kept for experiments)
-#endif
-
-// Logical XCDs the fused kernel splits the intermediate dimension over: the
-// chip's 8 when the device is a whole MI355X (256 CUs, 32 per XCD).  Any value
-// is correct; it only decides locality and balance.
-int fused_xcds(int cus) { return (cus >= 64 && cus % 8 == 0) ? 8 : 1; }
-
-// The fused kernel's LDS: x [T][Hp] + the XCD's h' slice [slots][T][Ix].
-size_t fused_lds(const LayerArgs &a, int slots, int nx) {
-  const size_t hp = (size_t)((a.H + kChunk - 1) / kChunk) * kChunk;
-  return (size_t)a.T * hp * sizeof(float) + (size_t)slots * a.T * (a.I / nx) * sizeof(float);
-}
-
-bool fused_ok(const LayerArgs &a, int slots, int nx) {
-  if (a.T > 2 || a.I % nx) return false;
-  const int ix = a.I / nx;
-  if (ix < 64 || ix > 1024 || (ix & (ix - 1))) return false;
-  if (a.n_shards != 1) {
-    const int w = a.I / a.n_shards;  // a power of two in [64, 1024] (check_shards)
-    if (w > ix) return false;       // a shard spanning XCDs needs a cross-XCD reduce
-  }
-  return fused_lds(a, slots, nx) <= 150 * 1024;
-}
-
-template <int T>
-hipError_t launch_fused_t(const LayerArgs &a, int slots, int nx, FuArgs f, hipStream_t st) {
-  constexpr int WA = DUCKMOE_FU_WAVES;
-  const auto kern = k_fused<T, WA>;
-  const size_t lds = fused_lds(a, slots, nx);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
-  int per_cu = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WA * 64, lds);
-  if (err != hipSuccess) return err;
-  const int cus = device_cus();
-  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
-  per_cu = std::max(1, std::min(per_cu, DUCKMOE_FU_WAVES_PER_CU / WA));
-  int grid = cus * per_cu;
-  grid -= grid % nx;
-  if (grid / nx > kFuMaxBlocks) grid = kFuMaxBlocks * nx;
-  const int ix = a.I / nx;
-  f.G = (a.n_shards == 1) ? ix / 16 : (a.I / a.n_shards) / 16;
-  f.n_xcd = nx;
-  if (DUCKMOE_FU_COOPERATIVE) {
-    LayerArgs aa = a;
-    void *args[] = {&aa, &f};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern), dim3(grid),
-                                      dim3(WA * 64), args, (unsigned)lds, st);
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), lds, st, a, f);
-  return hipGetLastError();
-}
-
 enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
 
 // Shared argument checks and dispatch of the layer entry points.
@@ -1373,19 +888,6 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   a.hdr = reinterpret_cast<WsHeader *>(ws);
   a.hbuf = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes);
 
-  if (DUCKMOE_FUSED && stages == kBoth) {
-    const int slots = (int)hbuf_slots(L, T, single);
-    const int nx = fused_xcds(device_cus());
-    if (fused_ok(a, slots, nx)) {
-      FuArgs f;
-      f.hdr = reinterpret_cast<uint8_t *>(ws);
-      f.Y = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes +
-                                      hbuf_bytes(L, T, single));
-      const hipError_t err = T == 1 ? launch_fused_t<1>(a, slots, nx, f, stream)
-                                    : launch_fused_t<2>(a, slots, nx, f, stream);
-      return err == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
-    }
-  }
   if (stages & kGateUp) {
     if (launch_gate_up(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   }
@@ -1482,7 +984,7 @@ int duckmoe_moe_plan(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_rou
   a.T = T;
   a.top_k = top_k;
   a.n_routed = n_routed;
-  a.w = nullptr;  // the slot list needs no weights; build_plan skips them
+  a.w = nullptr;  // the slot list needs no weights
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, stream, a, uniq, n_slots);
   return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
 }

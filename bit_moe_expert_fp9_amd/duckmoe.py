@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libduckmoe.so")
 
 OK, EINVAL, ESHAPE, ENONFINITE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
-STATUS_BAD_ID, STATUS_DUP_ID, STATUS_TIMEOUT = 1, 2, 4
+STATUS_BAD_ID, STATUS_DUP_ID = 1, 2
 MAX_TOKENS = 8
 
 _lib = None
@@ -200,9 +200,9 @@ class Layer:
         return n
 
     def workspace(self, T, n_shards=1):
-        """A zero-filled device workspace (the library needs it zeroed once)."""
+        """A device workspace for T tokens (needs no initialisation)."""
         import torch
-        return torch.zeros(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
+        return torch.empty(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
                            device=self.gu_body.device)
 
 
@@ -283,7 +283,8 @@ def gemv_fp9(body, sign, x, out=None, stream=None):
 
 
 def moe_plan(ids, n_routed, stream=None):
-    """Device expert-selection plan -> list of expert indices (shared last)."""
+    """Device expert-selection plan -> expert indices in slot order (shared
+    first, then the distinct valid ids by first appearance)."""
     import torch
     T, k = ids.shape
     uniq = torch.full((T * k + 1,), -1, dtype=torch.int32, device=ids.device)

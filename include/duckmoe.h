@@ -54,8 +54,6 @@ extern "C" {
 /* Bits of the device status word (duckmoe_status). */
 #define DUCKMOE_STATUS_BAD_ID  1  /* a routed id outside [0, n_routed): entry skipped   */
 #define DUCKMOE_STATUS_DUP_ID  2  /* a token lists an id twice: its weights were added  */
-#define DUCKMOE_STATUS_TIMEOUT 4  /* a bounded in-kernel wait expired: output invalid;
-                                     zero-fill the workspace before reusing it         */
 
 #define DUCKMOE_MAX_TOKENS 8      /* T, tokens per call                                 */
 #define DUCKMOE_MAX_IDS    64     /* T * top_k                                          */
@@ -107,11 +105,10 @@ int duckmoe_quantize_fp9(const float *w, int64_t rows, int64_t cols,
 /*
  * Bytes of device workspace duckmoe_expert_ffn / duckmoe_moe_layer need for T
  * tokens (the same figure covers both).  Returns 0 if the arguments are
- * invalid.  The workspace holds the status word, synchronisation counters, the
- * per-(expert, token) SwiGLU activations (f32) and per-XCD partial outputs.
- * A workspace must be zero-filled once before its first use; every call leaves
- * its counters at zero again.  Calls that may run at the same time need
- * separate workspaces.
+ * invalid.  The workspace holds the status word, the expert-selection plan
+ * and the per-(expert, token) SwiGLU activations (f32).  It needs no
+ * initialisation: every call writes what it later reads.  Calls that may run
+ * at the same time need separate workspaces.
  */
 size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shards);
 
@@ -190,8 +187,10 @@ int duckmoe_gemv_fp9(const uint8_t *body, const uint8_t *sign, int32_t rows, int
                      const float *x, float *y, hipStream_t stream);
 
 /*
- * [route] Expert-selection plan: the ascending distinct valid ids of
- * ids[T][top_k], then n_routed (the shared expert).
+ * [route] Expert-selection plan, in the slot order the layer kernels use:
+ * n_routed (the shared expert) first, then the distinct valid ids of
+ * ids[T][top_k] in order of first appearance (token-major).  Invalid ids
+ * (outside [0, n_routed)) are left out.
  *   uniq [T*top_k+1] int32 device <- plan entries (the rest untouched)
  *   n_slots [1] int32 device      <- number of entries written (distinct + 1)
  */

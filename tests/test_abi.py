@@ -66,9 +66,9 @@ def fake_layer(H=7168, I=2048, E=256, k=8):
 def test_workspace_bytes(L):
     lay = fake_layer()
     f = L.duckmoe_workspace_bytes
-    # header + h' [T*top_k+1][T][I] + XCD partials [8][T][H], all f32
-    assert f(ctypes.byref(lay), 1, 1) == 16384 + 9 * 1 * 2048 * 4 + 8 * 1 * 7168 * 4
-    assert f(ctypes.byref(lay), 2, 32) == 16384 + 17 * 2 * 2048 * 4 + 8 * 2 * 7168 * 4
+    # 1 KiB header (status, plan) + h' [T*top_k+1][T][I] f32
+    assert f(ctypes.byref(lay), 1, 1) == 1024 + 9 * 1 * 2048 * 4
+    assert f(ctypes.byref(lay), 2, 32) == 1024 + 17 * 2 * 2048 * 4
     assert f(ctypes.byref(lay), 0, 1) == 0
     assert f(ctypes.byref(lay), 9, 1) == 0
     assert f(ctypes.byref(lay), 1, 3) == 0      # 2048 / 3 not integral

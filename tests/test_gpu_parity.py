@@ -126,8 +126,8 @@ SMALL = [
     # (workload, H, I, n_routed, top_k): ragged last chunk in both GEMVs
     (100, 1040, 336, 24, 8),
     (101, 2064, 1536, 16, 4),
-    # intermediate sizes whose per-XCD slice is a power of two (single-launch
-    # path at T <= 2): slices of 64 and 128 columns, ragged hidden chunk
+    # power-of-two intermediate sizes below one chunk per shard (shard slices of
+    # 64..512 columns), ragged hidden chunk
     (102, 1040, 512, 20, 8),
     (103, 2064, 1024, 12, 6),
 ]
@@ -143,6 +143,18 @@ def small_layers(torch_dev):
     return out
 
 
+def expected_status(ids, n_routed):
+    """The status bits a layer call must report for these ids."""
+    st = 0
+    for row in np.asarray(ids):
+        valid = [int(i) for i in row if 0 <= i < n_routed]
+        if len(valid) < len(row):
+            st |= dm.duckmoe.STATUS_BAD_ID
+        if len(set(valid)) < len(valid):
+            st |= dm.duckmoe.STATUS_DUP_ID
+    return st
+
+
 def run_layer_case(torch, lay, ox, wl, step, T, n_shards=1, ids=None, w=None):
     H = lay.hidden
     x = synth.activations(SEED, wl, 0, step, T, H)
@@ -154,7 +166,7 @@ def run_layer_case(torch, lay, ox, wl, step, T, n_shards=1, ids=None, w=None):
     out = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids.astype(np.int32)),
                        to_dev(torch, w.astype(np.float32)), n_shards=n_shards, ws=ws)
     torch.cuda.synchronize()
-    assert dm.status(ws) & dm.duckmoe.STATUS_TIMEOUT == 0
+    assert dm.status(ws) == expected_status(ids, lay.n_routed)
     return x, ids, w, out.cpu().numpy()
 
 
@@ -173,26 +185,26 @@ def test_small_layer_all_batch_sizes(torch_dev, small_layers, wl, T):
 
 @pytest.mark.parametrize("n_shards", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("T", [1, 2])
-def test_small_layer_fused_shards(torch_dev, small_layers, n_shards, T):
-    """I = 1024 split 8 ways (128-column slices): shards of 512 / 256 span
-    several slices (two-launch path), 128 / 64 lie inside one."""
+def test_small_layer_pow2_shards(torch_dev, small_layers, n_shards, T):
+    """I = 1024: shard slices of 1024 down to 64 columns, each reduced by lane
+    groups as wide as the slice."""
     torch = torch_dev
     lay, ox = small_layers[103]
-    say("fused-size layer, T =", T, "n_shards =", n_shards)
+    say("I=1024 layer, T =", T, "n_shards =", n_shards)
     ws = lay.workspace(T, n_shards)
     x = synth.activations(SEED, 103, 0, 300 + n_shards, T, lay.hidden)
     ids, w = synth.routing(SEED, 103, 0, 300 + n_shards, T, lay.n_routed, lay.top_k)
     ox.prefetch(list(ids.ravel()) + [lay.n_routed])
-    for rep in range(2):  # the second call reuses the workspace's counters
+    for rep in range(2):  # the second call reuses the workspace
         got = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w),
                            n_shards=n_shards, ws=ws).cpu().numpy()
         assert dm.status(ws) == 0
         if n_shards == 1:
-            check_close(got, oracle.moe_layer(ox, x, ids, w, lay.n_routed), "fused T=%d" % T)
+            check_close(got, oracle.moe_layer(ox, x, ids, w, lay.n_routed), "I=1024 T=%d" % T)
         else:
             ref = oracle.moe_partials(ox, x, ids, w, lay.n_routed, n_shards)
             for r in range(n_shards):
-                check_close(got[r], ref[r], "fused shard %d/%d" % (r, n_shards))
+                check_close(got[r], ref[r], "I=1024 shard %d/%d" % (r, n_shards))
 
 
 @pytest.mark.parametrize("n_shards", [2, 3, 6, 12, 24])
@@ -215,17 +227,38 @@ def test_small_layer_shard_partials(torch_dev, small_layers, n_shards):
     check_close(got.sum(axis=0), full, "sum of %d partials" % n_shards)
 
 
+def first_appearance(ids, n_routed):
+    """Distinct valid ids in order of first appearance (token-major)."""
+    seen = []
+    for i in np.asarray(ids).ravel():
+        if 0 <= i < n_routed and int(i) not in seen:
+            seen.append(int(i))
+    return seen
+
+
 def test_plan_bit_exact(torch_dev):
+    """The device plan names the oracle's experts, each once, in the documented
+    slot order: the shared expert, then the routed ids by first appearance."""
     torch = torch_dev
     rng = np.random.default_rng(17)
     for T, k, E in [(1, 8, 256), (2, 8, 256), (8, 8, 256), (3, 5, 7), (8, 8, 8192), (1, 1, 1)]:
         say("plan", T, k, E)
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
         got = dm.moe_plan(to_dev(torch, ids), E)
-        assert got == oracle.moe_plan(ids, E)
+        ref = oracle.moe_plan(ids, E)  # ascending routed ids, shared last
+        assert got[0] == E
+        assert sorted(got[1:]) == ref[:-1]
+        assert got[1:] == first_appearance(ids, E)
     # overlapping sets across tokens: the union is streamed once
     ids = np.array([[5, 3, 9, 1], [3, 7, 1, 0]], dtype=np.int32)
-    assert dm.moe_plan(to_dev(torch, ids), 10) == [0, 1, 3, 5, 7, 9, 10]
+    assert dm.moe_plan(to_dev(torch, ids), 10) == [10, 5, 3, 9, 1, 7, 0]
+    # 64 distinct ids fill every lane of the plan
+    ids = rng.permutation(300)[:64].reshape(8, 8).astype(np.int32)
+    got = dm.moe_plan(to_dev(torch, ids), 300)
+    assert got == [300] + [int(i) for i in ids.ravel()]
+    # invalid ids are skipped, repeats keep their first slot
+    ids = np.array([[4, -1, 4, 2], [9, 2, 12, 4]], dtype=np.int32)
+    assert dm.moe_plan(to_dev(torch, ids), 10) == [10, 4, 2, 9]
 
 
 def test_bad_and_duplicate_ids(torch_dev, small_layers):
