@@ -179,11 +179,13 @@ def moe_partials(get_expert, x, ids, w, n_routed, n_shards):
     return np.stack(res)
 
 
-def rms_normalize(v):
-    """Glue between stacked layers: v / sqrt(mean(v^2)) per token, float64.
+def rms_normalize(v, eps=0.0):
+    """Glue between stacked layers: v / sqrt(mean(v^2) + eps) per token, float64.
 
-    Not on the pages' MoE path (their GPU stage normalises between layers);
-    used only to chain layers without overflow.
+    Not on the pages' MoE path (their GPU stage normalises between layers:
+    chapter page "第 9 章 MTP1 dual-lane overlap", section 9.5); used only to
+    chain layers without overflow.  eps = 0 is the plain reading; a positive
+    eps is the usual RMSNorm guard against an all-zero row.
     """
     V = np.atleast_2d(np.asarray(v, dtype=np.float64))
-    return V / np.sqrt(np.mean(V * V, axis=1, keepdims=True))
+    return V / np.sqrt(np.mean(V * V, axis=1, keepdims=True) + float(eps))

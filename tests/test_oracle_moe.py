@@ -228,3 +228,24 @@ def test_rms_normalize():
     r = oracle.rms_normalize(v)
     np.testing.assert_allclose(np.mean(r * r, axis=1), 1.0, rtol=1e-14)
     np.testing.assert_allclose(r * np.sqrt(np.mean(v * v, axis=1, keepdims=True)), v, rtol=1e-14)
+
+
+def test_rms_normalize_closed_forms():
+    # (3, 4): mean square 12.5; with eps = 0.5 it becomes 13
+    np.testing.assert_allclose(oracle.rms_normalize([3.0, 4.0]), [[3 / 12.5 ** 0.5, 4 / 12.5 ** 0.5]],
+                               rtol=1e-15)
+    np.testing.assert_allclose(oracle.rms_normalize([3.0, 4.0], eps=0.5),
+                               [[3 / 13 ** 0.5, 4 / 13 ** 0.5]], rtol=1e-15)
+    # a constant row c maps to c / sqrt(c^2 + eps): +-1 without eps
+    np.testing.assert_array_equal(oracle.rms_normalize(np.full((1, 7), -2.5)), -np.ones((1, 7)))
+    np.testing.assert_allclose(oracle.rms_normalize(np.full((1, 7), 2.0), eps=5.0), np.full((1, 7), 2 / 3),
+                               rtol=1e-15)
+    # invariant to a positive scale, odd in the sign, rows independent
+    v = RNG.standard_normal((2, 33))
+    np.testing.assert_allclose(oracle.rms_normalize(1024.0 * v), oracle.rms_normalize(v), rtol=1e-14)
+    np.testing.assert_array_equal(oracle.rms_normalize(-v), -oracle.rms_normalize(v))
+    np.testing.assert_array_equal(oracle.rms_normalize(v)[1], oracle.rms_normalize(v[1:])[0])
+    # an all-zero row: 0/0 without eps, 0 with it
+    with np.errstate(invalid="ignore"):
+        assert np.all(np.isnan(oracle.rms_normalize(np.zeros((1, 4)))))
+    np.testing.assert_array_equal(oracle.rms_normalize(np.zeros((1, 4)), eps=1e-6), np.zeros((1, 4)))
