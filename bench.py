@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=4,
                    help="tokens (bsz 1 steps) the oracle times for the CPU baseline")
     p.add_argument("--bsz2", type=int, default=1, help="also time bsz 2 (0 to skip)")
+    p.add_argument("--stack", action="store_true",
+                   help="also time the 16-layer stack (about 204 GB of fp9 weights drawn on the "
+                        "device) at bsz 1, 2, 4 and 8; results go under 'stack'")
+    p.add_argument("--stack-steps", type=int, default=100)
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="first run 3 plain device copies of this many MiB (a known-size "
                         "reference for HBM byte counters under rocprofv3 --pmc)")
@@ -187,6 +191,68 @@ def time_stages(torch, dm, layer, T, steps, warmup, draws):
     }
 
 
+STACK_LAYERS, STACK_WORKLOAD = 16, 5
+
+
+def time_stack(torch, dm, steps, warmup):
+    """Stack passes (16 layers + RMS glue, one native call each) at bsz 1, 2, 4, 8."""
+    from bit_moe_expert_fp9_amd import synth
+    t0 = time.time()
+    layers = [dm.Layer(H, I, E, K).fill_synthetic_device(SEED, STACK_WORKLOAD, l)
+              for l in range(STACK_LAYERS)]
+    torch.cuda.synchronize()
+    log("stack of %d layers drawn on the device in %.1f s" % (STACK_LAYERS, time.time() - t0))
+    stack = dm.Stack(layers)
+    eb = layers[0].expert_bytes()
+    stream = torch.cuda.current_stream()
+    res = {}
+    for T in (1, 2, 4, 8):
+        n = steps + warmup
+        X, IDS, W, by = [], [], [], []
+        for s in range(n):
+            X.append(synth.activations(SEED, STACK_WORKLOAD, 0, 40_000 + s, T, H))
+            r = [synth.routing(SEED, STACK_WORKLOAD, l, 40_000 + s, T, E, K)
+                 for l in range(STACK_LAYERS)]
+            IDS.append(np.stack([a for a, _ in r]))
+            W.append(np.stack([b for _, b in r]))
+            by.append(sum((len(np.unique(a)) + 1) * eb for a, _ in r))
+        X = torch.from_numpy(np.stack(X)).cuda()
+        IDS = torch.from_numpy(np.stack(IDS).astype(np.int32)).cuda()
+        W = torch.from_numpy(np.stack(W).astype(np.float32)).cuda()
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        ws = stack.workspace(T)
+        for s in range(warmup):
+            dm.moe_stack(stack, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k in range(steps):
+            s = warmup + k
+            dm.moe_stack(stack, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        if not np.all(np.isfinite(out.cpu().numpy())):
+            raise RuntimeError("non-finite stack output at bsz %d" % T)
+        gb = float(np.mean(by[warmup:])) / 1e9
+        res[str(T)] = {
+            "ms_per_pass": ms,
+            "tokens_per_s": T / (ms * 1e-3),
+            "layer_tokens_per_s": T * STACK_LAYERS / (ms * 1e-3),
+            "gb_per_pass": gb,
+            "hbm_gbps": gb / (ms * 1e-3),
+            "hbm_frac": gb / (ms * 1e-3) / HBM_PEAK_GBPS,
+        }
+        log("stack bsz%d:" % T, json.dumps(res[str(T)]))
+        del X, IDS, W, ws
+    del stack, layers
+    torch.cuda.empty_cache()
+    return {"layers": STACK_LAYERS, "workload": "16 distinct fp9 layers (7168/2048, 256 routed + "
+            "1 shared, top-8), RMS glue between layers, one native call per pass",
+            "weights": "N(0, 0.02) drawn on the device, quantized by the device quantizer",
+            "steps": steps, "by_bsz": res}
+
+
 def cpu_baseline(n_tokens):
     """The float64 oracle on `n_tokens` bsz-1 steps of the same layer (1 thread)."""
     import oracle
@@ -293,6 +359,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.stack:
+        res["stack"] = time_stack(torch, dm, args.stack_steps, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(res), flush=True)

@@ -12,6 +12,7 @@ from .duckmoe import (  # noqa: F401
     LIB_PATH,
     Layer,
     LayerStruct,
+    Stack,
     decode_fp9,
     expert_ffn,
     gemv_fp9,
@@ -20,7 +21,10 @@ from .duckmoe import (  # noqa: F401
     moe_gate_up,
     moe_layer,
     moe_plan,
+    moe_stack,
     quantize_fp9,
+    quantize_fp9_device,
+    rms_normalize,
     status,
     strerror,
 )

@@ -87,6 +87,8 @@ struct LayerArgs {
   float *out;
   WsHeader *hdr;
   float *hbuf;         // h' [slot][t][I]
+  int in_rms;          // 1: normalize each x row by its RMS first (stack glue)
+  float in_eps;
 };
 
 // ----------------------------------------------------------------- plan ----
@@ -207,6 +209,22 @@ __device__ __forceinline__ void plan_store(const WavePlan &p, const LayerArgs &a
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// The RMS glue's sum of squares of one row in a fixed order: thread j < 256
+// adds x[j], x[j + 256], ... with fused multiply-adds; each of the 4 waves sums
+// its lanes; the 4 wave sums are added as (w0 + w1) + (w2 + w3) by rms_divisor.
+// k_rms and the gate/up prologue both use it, so normalizing inside the layer
+// gives the same bits as normalizing before it.
+__device__ __forceinline__ float rms_wave_part(const float *row, int H) {
+  float ss = 0.0f;
+  if (threadIdx.x < 256)
+    for (int i = threadIdx.x; i < H; i += 256) ss = __builtin_fmaf(row[i], row[i], ss);
+  return wave_sum(ss);
+}
+
+__device__ __forceinline__ float rms_divisor(const float part[4], int H, float eps) {
+  return sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H + eps);
+}
 
 // ------------------------------------------------------------- gate / up ----
 // Persistent: grid = resident workgroups, WA waves each.  The tasks are
@@ -387,6 +405,22 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
 #pragma unroll 4
   for (int q = threadIdx.x + XR * NT; q < n4; q += NT) xs4[q] = buf_loadf4(rx, x_off(q));
   __syncthreads();
+  if (a.in_rms) {  // stack glue: x[t] /= sqrt(mean x[t]^2 + eps), in LDS
+    __shared__ float part[TG][4];
+    float *xs = reinterpret_cast<float *>(xs4);
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float ss = rms_wave_part(xs + t * Hp4 * 4, H);
+      if (lane == 0 && wave < 4) part[t][wave] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float r = rms_divisor(part[t], H, a.in_eps);
+      for (int i = threadIdx.x; i < H; i += NT) xs[t * Hp4 * 4 + i] /= r;
+    }
+    __syncthreads();
+  }
 
   float acc[2][P][TG][2];
 #pragma unroll
@@ -695,6 +729,20 @@ __global__ __launch_bounds__(64) void k_plan(const LayerArgs a, int32_t *uniq, i
   if (lane < p.n_slots - 1) uniq[1 + lane] = p.expert;
 }
 
+// y[t] = x[t] / sqrt(mean_i x[t][i]^2 + eps): one workgroup of 256 threads per
+// token, sum of squares in f32 in the order of rms_wave_part; every element is
+// read before any is written, so y may be x.
+__global__ __launch_bounds__(256) void k_rms(const float *x, int H, float eps, float *y) {
+  __shared__ float part[4];
+  const float *xr = x + (size_t)blockIdx.x * H;
+  float *yr = y + (size_t)blockIdx.x * H;
+  const float ss = rms_wave_part(xr, H);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = rms_divisor(part, H, eps);
+  for (int i = threadIdx.x; i < H; i += 256) yr[i] = xr[i] / r;
+}
+
 // ------------------------------------------------------------ host side ----
 bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
@@ -855,7 +903,8 @@ enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
 // Shared argument checks and dispatch of the layer entry points.
 int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const float *w,
               int single_expert, int32_t T, float *out, int32_t n_shards, void *ws,
-              size_t ws_bytes, hipStream_t stream, int stages) {
+              size_t ws_bytes, hipStream_t stream, int stages, int in_rms = 0,
+              float in_eps = 0.0f) {
   int rc = check_layer(L);
   if (rc) return rc;
   const bool single = ids == nullptr;
@@ -887,6 +936,8 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   a.out = out;
   a.hdr = reinterpret_cast<WsHeader *>(ws);
   a.hbuf = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + kHdrBytes);
+  a.in_rms = in_rms;
+  a.in_eps = in_eps;
 
   if (stages & kGateUp) {
     if (launch_gate_up(a, stream) != hipSuccess) return DUCKMOE_EHIP;
@@ -936,6 +987,69 @@ int duckmoe_expert_ffn(const duckmoe_layer *L, int32_t e, const float *x, int32_
                        float *out, int32_t n_shards, void *ws, size_t ws_bytes,
                        hipStream_t stream) {
   return run_layer(L, x, nullptr, nullptr, e, T, out, n_shards, ws, ws_bytes, stream, kBoth);
+}
+
+int duckmoe_rms_normalize(const float *x, int32_t T, int32_t H, float eps, float *y,
+                          hipStream_t stream) {
+  if (!x || !y || T < 0 || H < 1 || !(eps >= 0.0f)) return DUCKMOE_EINVAL;
+  if (T == 0) return DUCKMOE_OK;
+  hipLaunchKernelGGL(k_rms, dim3(T), dim3(256), 0, stream, x, H, eps, y);
+  return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+// stack workspace: one layer's workspace, then two [T][H] activation buffers
+static size_t stack_act_off(const duckmoe_layer *L, int T) {
+  return (ws_need(L, T, false) + 255) / 256 * 256;
+}
+
+static size_t stack_act_bytes(const duckmoe_layer *L, int T) {
+  return ((size_t)T * L->hidden * sizeof(float) + 255) / 256 * 256;
+}
+
+static int check_stack(const duckmoe_layer *layers, int32_t n_layers, int32_t T) {
+  if (!layers || n_layers < 1 || T < 1 || T > kMaxT) return DUCKMOE_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    const int rc = check_layer(&layers[l]);
+    if (rc) return rc;
+    const duckmoe_layer &a = layers[0], &b = layers[l];
+    if (b.hidden != a.hidden || b.inter != a.inter || b.n_routed != a.n_routed ||
+        b.top_k != a.top_k)
+      return DUCKMOE_ESHAPE;
+  }
+  if (T * layers[0].top_k > kMaxIds) return DUCKMOE_ESHAPE;
+  return DUCKMOE_OK;
+}
+
+size_t duckmoe_stack_workspace_bytes(const duckmoe_layer *layers, int32_t n_layers, int32_t T) {
+  if (check_stack(layers, n_layers, T)) return 0;
+  return stack_act_off(&layers[0], T) + 2 * stack_act_bytes(&layers[0], T);
+}
+
+int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float *x,
+                      const int32_t *ids, const float *w, int32_t T, float eps, float *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_stack(layers, n_layers, T);
+  if (rc) return rc;
+  if (!x || !ids || !w || !out || !ws || !(eps >= 0.0f)) return DUCKMOE_EINVAL;
+  if (!aligned(ws, 256)) return DUCKMOE_EINVAL;
+  const duckmoe_layer *L0 = &layers[0];
+  if (ws_bytes < duckmoe_stack_workspace_bytes(layers, n_layers, T)) return DUCKMOE_EWORKSPACE;
+  uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+  float *act[2] = {reinterpret_cast<float *>(base + stack_act_off(L0, T)),
+                   reinterpret_cast<float *>(base + stack_act_off(L0, T) +
+                                             stack_act_bytes(L0, T))};
+  // Layer l > 0 reads layer l-1's raw output and normalizes it in its gate/up
+  // prologue (bit-identical to duckmoe_rms_normalize followed by the layer).
+  const size_t per = (size_t)T * L0->top_k;
+  const float *in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    float *y = l == n_layers - 1 ? out : act[l & 1];
+    rc = run_layer(&layers[l], in, ids + l * per, w + l * per, 0, T, y, 1, ws,
+                   stack_act_off(L0, T), stream, kBoth, l > 0, eps);
+    if (rc) return rc;
+    in = y;
+  }
+  return DUCKMOE_OK;
 }
 
 int duckmoe_status(const void *ws, int32_t *status, hipStream_t stream) {

@@ -61,6 +61,11 @@ _SIGNATURES = {
     "duckmoe_decode_fp9": ([_P, _P, _I64, _P, _P], ctypes.c_int),
     "duckmoe_gemv_fp9": ([_P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "duckmoe_moe_plan": ([_P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "duckmoe_quantize_fp9_device": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "duckmoe_rms_normalize": ([_P, _I32, _I32, ctypes.c_float, _P, _P], ctypes.c_int),
+    "duckmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
+    "duckmoe_moe_stack": ([ctypes.POINTER(LayerStruct), _I32, _P, _P, _P, _I32, ctypes.c_float,
+                           _P, _P, _SZ, _P], ctypes.c_int),
 }
 
 EXPORTS = tuple(_SIGNATURES)
@@ -137,6 +142,28 @@ def quantize_fp9(w, body=None, sign=None):
     return body, sign
 
 
+def quantize_fp9_device(w, body=None, sign=None, nonfinite=None, stream=None):
+    """Device float32 [rows, cols] -> (body uint8, sign uint8) on the GPU.
+
+    `body`/`sign` may be preallocated device tensors (flat or shaped, with at
+    least rows*cols and rows*cols/8 elements from their start); `nonfinite`, a
+    device int32 tensor, is set to 1 if w holds a NaN.
+    """
+    import torch
+    _need_device(w, torch.float32, "w")
+    rows, cols = w.shape
+    if body is None:
+        body = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    if sign is None:
+        sign = torch.empty((rows, max(cols // 8, 0)), dtype=torch.uint8, device=w.device)
+    if body.numel() < rows * cols or sign.numel() < rows * (cols // 8):
+        raise ValueError("body/sign too small")
+    _check(lib().duckmoe_quantize_fp9_device(_ptr(w), rows, cols, _ptr(body), _ptr(sign),
+                                             _ptr(nonfinite), _stream(stream)),
+           "duckmoe_quantize_fp9_device")
+    return body, sign
+
+
 # ----------------------------------------------------------------- layer ----
 
 class Layer:
@@ -174,6 +201,31 @@ class Layer:
         self.gu_sign[e * 2 * mat // 8:(e + 1) * 2 * mat // 8].copy_(torch.from_numpy(gs.reshape(-1)))
         self.dn_body[e * mat:(e + 1) * mat].copy_(torch.from_numpy(db.reshape(-1)))
         self.dn_sign[e * mat // 8:(e + 1) * mat // 8].copy_(torch.from_numpy(dsn.reshape(-1)))
+
+    def set_expert_device(self, e, gate, up, down, nonfinite=None, stream=None):
+        """Quantize device float32 matrices (gate/up [I,H], down [H,I]) into
+        expert e with the device quantizer (asynchronous on `stream`)."""
+        H, I = self.hidden, self.inter
+        mat = I * H
+        for src, rows, body, sign in ((gate, I, self.gu_body[e * 2 * mat:], self.gu_sign[e * 2 * mat // 8:]),
+                                      (up, I, self.gu_body[(e * 2 + 1) * mat:],
+                                       self.gu_sign[(e * 2 + 1) * mat // 8:]),
+                                      (down, H, self.dn_body[e * mat:], self.dn_sign[e * mat // 8:])):
+            quantize_fp9_device(src, body=body, sign=sign, nonfinite=nonfinite, stream=stream)
+
+    def fill_synthetic_device(self, seed, workload, layer):
+        """Draw every expert with synth.weights_device and quantize it on the GPU."""
+        import torch
+        H, I = self.hidden, self.inter
+        flag = torch.zeros(1, dtype=torch.int32, device=self.gu_body.device)
+        for e in range(self.n_experts):
+            g = synth.weights_device(seed, workload, layer, e, synth.GATE, (I, H), self.gu_body.device)
+            u = synth.weights_device(seed, workload, layer, e, synth.UP, (I, H), self.gu_body.device)
+            d = synth.weights_device(seed, workload, layer, e, synth.DOWN, (H, I), self.gu_body.device)
+            self.set_expert_device(e, g, u, d, nonfinite=flag)
+        if int(flag.item()):
+            raise DuckMoeError(ENONFINITE, "fill_synthetic_device")
+        return self
 
     def fill_synthetic(self, seed, workload, layer, threads=None):
         """Draw every expert from synth.weights and upload it (threaded)."""
@@ -249,6 +301,53 @@ def expert_ffn(layer, e, x, out=None, n_shards=1, ws=None, stream=None):
     rc = lib().duckmoe_expert_ffn(ctypes.byref(layer.struct), e, _ptr(x), T, _ptr(out),
                                   n_shards, _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "duckmoe_expert_ffn")
+    return out
+
+
+def rms_normalize(x, eps=0.0, out=None, stream=None):
+    """y[t] = x[t] / sqrt(mean(x[t]^2) + eps) on the device (x [T, H] float32)."""
+    import torch
+    _need_device(x, torch.float32, "x")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().duckmoe_rms_normalize(_ptr(x), T, H, float(eps), _ptr(out), _stream(stream)),
+           "duckmoe_rms_normalize")
+    return out
+
+
+class Stack:
+    """A chain of equally shaped layers run by duckmoe_moe_stack."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.structs = (LayerStruct * len(self.layers))(*[l.struct for l in self.layers])
+
+    def workspace(self, T):
+        import torch
+        n = lib().duckmoe_stack_workspace_bytes(self.structs, len(self.layers), T)
+        if n == 0:
+            raise DuckMoeError(EINVAL, "duckmoe_stack_workspace_bytes")
+        return torch.empty(n, dtype=torch.uint8, device=self.layers[0].gu_body.device)
+
+
+def moe_stack(stack, x, ids, w, eps=0.0, out=None, ws=None, stream=None):
+    """Run every layer of `stack` with the RMS glue in between (see the header).
+
+    x [T, H] float32; ids int32 / w float32 [n_layers, T, top_k]; device tensors.
+    """
+    import torch
+    _need_device(x, torch.float32, "x")
+    _need_device(ids, torch.int32, "ids")
+    _need_device(w, torch.float32, "w")
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = stack.workspace(T)
+    _check(lib().duckmoe_moe_stack(stack.structs, len(stack.layers), _ptr(x), _ptr(ids), _ptr(w),
+                                   T, float(eps), _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "duckmoe_moe_stack")
     return out
 
 

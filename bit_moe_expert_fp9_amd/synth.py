@@ -13,6 +13,13 @@ prompts, neither available; these draws stand in, with the layer's shapes):
     experts, weights = softmax of top_k N(0, 1) draws, per
     (seed, workload, layer, step).
 Every stream is numpy's PCG64 seeded by SeedSequence of the tuple above.
+
+For layers too large to draw on the host in reasonable time (the 16-layer
+stack holds 4112 experts), weights_device draws the same N(0, 0.02)
+distribution on the GPU with torch's Philox generator, seeded from the same
+key.  It is a different stream from `weights` (the values differ); the oracle
+side takes those device-drawn float32 values, copied to the host, and
+quantizes them itself.
 """
 
 import numpy as np
@@ -32,6 +39,22 @@ def weights(seed, workload, layer, expert, matrix, shape, out=None):
         out = np.empty(shape, dtype=np.float32)
     rng.standard_normal(out=out, dtype=np.float32)
     out *= np.float32(WEIGHT_STD)
+    return out
+
+
+def device_seed(*key):
+    """63-bit torch generator seed derived from a key tuple."""
+    state = np.random.SeedSequence([int(k) for k in key]).generate_state(2, np.uint32)
+    return (int(state[0]) | (int(state[1]) << 32)) & ((1 << 63) - 1)
+
+
+def weights_device(seed, workload, layer, expert, matrix, shape, device="cuda"):
+    """N(0, 0.02) float32 of the given shape drawn on `device` (torch Philox)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(seed, workload, layer, expert, matrix, 3))
+    out = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    out.mul_(WEIGHT_STD)
     return out
 
 

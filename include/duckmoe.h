@@ -18,6 +18,10 @@
  *  [route] chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2
  *          "两条路线的判断": 8 routed experts per token (top_k = 8); the sets of
  *          two tokens barely overlap, so bsz 2 reads about twice the weights.
+ *  [lane]  chapter page "第 9 章 MTP1 dual-lane overlap", section 9.5
+ *          "pair runtime：stage0/stage1 调度": per decoder layer, a GPU stage
+ *          (attention, layernorm, residual add) precedes the FFN/MoE stage,
+ *          and layer i+1 of a lane waits for layer i's MoE result.
  *  [f32]   ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
  *          "形态一：Mac-to-Mac 张量并行（RDMA）": TP partial sums travel as f32.
  *
@@ -103,6 +107,21 @@ int duckmoe_quantize_fp9(const float *w, int64_t rows, int64_t cols,
                          uint8_t *body, uint8_t *sign);
 
 /*
+ * [fp9] The same quantizer and packer on the GPU (bit-identical results),
+ * asynchronous on `stream`; w, body, sign DEVICE pointers.
+ *   w    [rows][cols] float32, 16-byte aligned
+ *   body [rows][cols] uint8, 8-byte aligned;  sign [rows][cols/8] uint8
+ *   nonfinite: device int32 or NULL; set to 1 if any element is NaN (never
+ *              cleared by the call; the codes of NaN elements are unspecified)
+ * Errors (host-side, nothing launched): DUCKMOE_EINVAL for negative sizes or
+ * null or misaligned pointers, DUCKMOE_ESHAPE if cols % 8 != 0.  rows or
+ * cols == 0 is a no-op (the pointers may then be null).
+ */
+int duckmoe_quantize_fp9_device(const float *w, int64_t rows, int64_t cols,
+                                uint8_t *body, uint8_t *sign, int32_t *nonfinite,
+                                hipStream_t stream);
+
+/*
  * Bytes of device workspace duckmoe_expert_ffn / duckmoe_moe_layer need for T
  * tokens (the same figure covers both).  Returns 0 if the arguments are
  * invalid.  The workspace holds the status word, the expert-selection plan
@@ -160,6 +179,34 @@ int duckmoe_moe_down(const duckmoe_layer *L, const float *x, const int32_t *ids,
 int duckmoe_expert_ffn(const duckmoe_layer *L, int32_t e, const float *x, int32_t T,
                        float *out, int32_t n_shards, void *ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/*
+ * [lane] Glue between stacked layers: y[t] = x[t] / sqrt(mean_i x[t][i]^2 + eps)
+ * for t < T, i < H, in float32.  x, y [T][H] device float32 (y may equal x).
+ * DUCKMOE_EINVAL for null pointers, T < 0, H < 1 or eps < 0 (or NaN).  With
+ * eps = 0 an all-zero row gives 0/0 = NaN, as the formula does.
+ */
+int duckmoe_rms_normalize(const float *x, int32_t T, int32_t H, float eps, float *y,
+                          hipStream_t stream);
+
+/*
+ * [lane][afd] A stack of n_layers routed layers chained through the glue above:
+ *   h_0 = x;  y_l = moe_layer(layers[l], h_l, ids[l], w[l]);
+ *   h_{l+1} = rms_normalize(y_l, eps);  out = y_{n_layers-1}.
+ *   layers  host array of n_layers descriptors with equal hidden, inter,
+ *           n_routed and top_k (DUCKMOE_ESHAPE otherwise)
+ *   x [T][H], out [T][H] float32 device; ids, w [n_layers][T][top_k] device
+ *   ws      device workspace of duckmoe_stack_workspace_bytes(...) bytes,
+ *           256-byte aligned, needing no initialisation
+ * The status word (duckmoe_status on ws) is that of the last layer.  The glue
+ * runs inside the next layer's first kernel (no launch of its own) with the
+ * same arithmetic in the same order, so the result equals calling
+ * duckmoe_moe_layer and duckmoe_rms_normalize in turn, bit for bit.
+ */
+size_t duckmoe_stack_workspace_bytes(const duckmoe_layer *layers, int32_t n_layers, int32_t T);
+int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float *x,
+                      const int32_t *ids, const float *w, int32_t T, float eps, float *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Reads the status word the last layer call on this workspace wrote

@@ -32,16 +32,24 @@ class OracleExperts:
     """Oracle-side expert codes: the synthetic float32 weights quantized by the
     oracle's own quantizer (never by the library), cached per expert."""
 
-    def __init__(self, seed, workload, layer, hidden, inter):
+    def __init__(self, seed, workload, layer, hidden, inter, device_drawn=False):
+        """device_drawn: the layer's weights come from synth.weights_device (the
+        float32 draws are copied to the host; only the drawing is on the GPU)."""
         self.key = (seed, workload, layer)
         self.H, self.I = hidden, inter
+        self.device_drawn = device_drawn
         self.cache = {}
 
-    def _make(self, e):
+    def _draw(self, e, m, shape):
         s, wl, l = self.key
-        gate = synth.weights(s, wl, l, e, synth.GATE, (self.I, self.H))
-        up = synth.weights(s, wl, l, e, synth.UP, (self.I, self.H))
-        down = synth.weights(s, wl, l, e, synth.DOWN, (self.H, self.I))
+        if self.device_drawn:
+            return synth.weights_device(s, wl, l, e, m, shape).cpu().numpy()
+        return synth.weights(s, wl, l, e, m, shape)
+
+    def _make(self, e):
+        gate = self._draw(e, synth.GATE, (self.I, self.H))
+        up = self._draw(e, synth.UP, (self.I, self.H))
+        down = self._draw(e, synth.DOWN, (self.H, self.I))
         return (oracle.quantize(gate), oracle.quantize(up), oracle.quantize(down))
 
     def prefetch(self, experts):

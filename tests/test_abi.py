@@ -135,6 +135,48 @@ def test_building_block_errors(L):
     assert L.duckmoe_status(None, None, None) == E.EINVAL
 
 
+def test_device_quantizer_and_glue_errors(L):
+    E = dm.duckmoe
+    q = L.duckmoe_quantize_fp9_device
+    assert q(None, 2, 8, FAKE, FAKE, None, None) == E.EINVAL
+    assert q(FAKE, -1, 8, FAKE, FAKE, None, None) == E.EINVAL
+    assert q(FAKE, 2, 12, FAKE, FAKE, None, None) == E.ESHAPE
+    assert q(FAKE + 4, 2, 8, FAKE, FAKE, None, None) == E.EINVAL   # w 16-byte aligned
+    assert q(FAKE, 2, 8, FAKE + 4, FAKE, None, None) == E.EINVAL   # body 8-byte aligned
+    assert q(FAKE, 0, 8, FAKE, FAKE, None, None) == 0
+    assert q(None, 0, 8, None, None, None, None) == 0
+    r = L.duckmoe_rms_normalize
+    assert r(None, 1, 16, 0.0, FAKE, None) == E.EINVAL
+    assert r(FAKE, -1, 16, 0.0, FAKE, None) == E.EINVAL
+    assert r(FAKE, 1, 0, 0.0, FAKE, None) == E.EINVAL
+    assert r(FAKE, 1, 16, -1.0, FAKE, None) == E.EINVAL
+    assert r(FAKE, 1, 16, float("nan"), FAKE, None) == E.EINVAL
+    assert r(FAKE, 0, 16, 0.0, FAKE, None) == 0
+
+
+def test_stack_errors(L):
+    E = dm.duckmoe
+    layers = (LayerStruct * 3)(fake_layer(), fake_layer(), fake_layer())
+    wsb = L.duckmoe_stack_workspace_bytes
+    one = 1024 + 9 * 2048 * 4
+    assert wsb(layers, 3, 1) == (one + 255) // 256 * 256 + 2 * 7168 * 4
+    assert wsb(layers, 0, 1) == 0
+    assert wsb(layers, 3, 9) == 0
+    assert wsb(None, 3, 1) == 0
+    mixed = (LayerStruct * 2)(fake_layer(), fake_layer(I=1024))
+    assert wsb(mixed, 2, 1) == 0
+    st = lambda lay, n=3, x=FAKE, ids=FAKE, w=FAKE, T=1, eps=0.0, out=FAKE, ws=FAKE, b=1 << 30: \
+        L.duckmoe_moe_stack(lay, n, x, ids, w, T, eps, out, ws, b, None)
+    assert st(mixed, 2) == E.ESHAPE
+    assert st(layers, 0) == E.EINVAL
+    assert st(layers, T=9) == E.EINVAL
+    assert st(layers, x=None) == E.EINVAL
+    assert st(layers, ids=None) == E.EINVAL
+    assert st(layers, eps=-1.0) == E.EINVAL
+    assert st(layers, ws=FAKE + 16) == E.EINVAL
+    assert st(layers, b=1000) == E.EWORKSPACE
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     from bit_moe_expert_fp9_amd import duckmoe
     monkeypatch.setattr(duckmoe, "_lib", None)
