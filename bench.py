@@ -34,8 +34,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "94537c48b3f09de32ad80e610155bb319e79890da04ca9fd8257a9b6c2cbec4d",
-    "bytes_per_launch": 297732859,
+    "sources_sha256": "6e198fc4d363586ef1bf533a043d57832267e9e5bc3f6d0660ada95beb2248b4",
+    "bytes_per_launch": 297766687,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h")
 
@@ -191,6 +191,32 @@ def time_stages(torch, dm, layer, T, steps, warmup, draws):
     }
 
 
+def read_ceiling(torch, dm, sizes, reps=100):
+    """Plain streaming-read time (duckmoe_read_probe) for each byte count, each
+    launch on a fresh window of an 8-window buffer (no reuse from the cache)."""
+    sizes = [s // 1024 * 1024 for s in sizes]
+    win = max(sizes)
+    buf = torch.empty(8 * win, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for nb in sizes:
+        for i in range(10):
+            dm.read_probe(buf[(i % 8) * win:], nb, sink, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev[2 * i].record(stream)
+            dm.read_probe(buf[((i * 3) % 8) * win:], nb, sink, stream=stream)
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)])) * 1e3
+        out[nb] = (us, nb / (us * 1e-6) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 STACK_LAYERS, STACK_WORKLOAD = 16, 5
 
 
@@ -320,6 +346,10 @@ def main():
     log("bsz1 stages:", json.dumps(st1))
 
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
+    ceil = read_ceiling(torch, dm, [int(r1["bytes_step"]), int(st1["gate_up_bytes"])])
+    (lay_b, (lay_us, lay_gbps)), (gu_b, (gu_us, gu_gbps)) = sorted(ceil.items(), reverse=True)
+    log("read ceiling: %d B in %.1f us (%.0f GB/s); %d B in %.1f us (%.0f GB/s)" %
+        (lay_b, lay_us, lay_gbps, gu_b, gu_us, gu_gbps))
     res = {
         "metric": METRIC,
         "value": r1["tokens_per_s"],
@@ -344,6 +374,11 @@ def main():
             "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
             "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
             "stages_us": {"k_gate_up": st1["gate_up_us"], "k_down": st1["down_us"]},
+            "read_ceiling": {"what": "plain streaming read of the same byte count, one launch, "
+                                     "fresh window, HIP events (duckmoe_read_probe)",
+                             "layer_bytes": lay_b, "layer_us": lay_us, "layer_gbps": lay_gbps,
+                             "gate_up_bytes": gu_b, "gate_up_us": gu_us, "gate_up_gbps": gu_gbps},
+            "layer_frac_of_read_ceiling": gbps / lay_gbps,
             "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {
@@ -356,6 +391,8 @@ def main():
             "avg_launch_us": st1["gate_up_us"],
             "bytes_per_launch": st1["gate_up_bytes"],
             "traffic": measured_traffic(),
+            "read_ceiling_gbps": gu_gbps,
+            "frac_of_read_ceiling": st1["gate_up_gbps"] / gu_gbps,
         },
         "cpu_baseline": None,
     }

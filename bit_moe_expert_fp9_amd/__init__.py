@@ -24,6 +24,7 @@ from .duckmoe import (  # noqa: F401
     moe_stack,
     quantize_fp9,
     quantize_fp9_device,
+    read_probe,
     rms_normalize,
     status,
     strerror,

@@ -61,6 +61,7 @@ _SIGNATURES = {
     "duckmoe_decode_fp9": ([_P, _P, _I64, _P, _P], ctypes.c_int),
     "duckmoe_gemv_fp9": ([_P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "duckmoe_moe_plan": ([_P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "duckmoe_read_probe": ([_P, _SZ, _P, _P], ctypes.c_int),
     "duckmoe_quantize_fp9_device": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "duckmoe_rms_normalize": ([_P, _I32, _I32, ctypes.c_float, _P, _P], ctypes.c_int),
     "duckmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
@@ -349,6 +350,12 @@ def moe_stack(stack, x, ids, w, eps=0.0, out=None, ws=None, stream=None):
                                    T, float(eps), _ptr(out), _ptr(ws), ws.numel(),
                                    _stream(stream)), "duckmoe_moe_stack")
     return out
+
+
+def read_probe(buf, nbytes, sink, stream=None):
+    """Plain streaming read of the first nbytes of device tensor buf (calibration)."""
+    _check(lib().duckmoe_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+           "duckmoe_read_probe")
 
 
 def status(ws, stream=None):

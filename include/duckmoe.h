@@ -244,6 +244,16 @@ int duckmoe_gemv_fp9(const uint8_t *body, const uint8_t *sign, int32_t rows, int
 int duckmoe_moe_plan(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_routed,
                      int32_t *uniq, int32_t *n_slots, hipStream_t stream);
 
+/*
+ * Calibration: a plain streaming read of `bytes` device bytes (16-byte
+ * aligned buf, bytes a multiple of 1024; DUCKMOE_EINVAL otherwise) with
+ * dwordx4 loads, 8 in flight per lane, 32 waves per CU.  It computes nothing
+ * of the method; its duration is the read ceiling that the weight-streaming
+ * kernels above are compared with.  sink: device uint32, written only in a case
+ * that does not occur (it keeps the loads alive).
+ */
+int duckmoe_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -154,6 +154,15 @@ def test_device_quantizer_and_glue_errors(L):
     assert r(FAKE, 0, 16, 0.0, FAKE, None) == 0
 
 
+def test_read_probe_errors(L):
+    E = dm.duckmoe
+    assert L.duckmoe_read_probe(None, 1024, FAKE, None) == E.EINVAL
+    assert L.duckmoe_read_probe(FAKE, 1000, FAKE, None) == E.EINVAL
+    assert L.duckmoe_read_probe(FAKE + 4, 1024, FAKE, None) == E.EINVAL
+    assert L.duckmoe_read_probe(FAKE, 1024, None, None) == E.EINVAL
+    assert L.duckmoe_read_probe(FAKE, 0, FAKE, None) == 0
+
+
 def test_stack_errors(L):
     E = dm.duckmoe
     layers = (LayerStruct * 3)(fake_layer(), fake_layer(), fake_layer())

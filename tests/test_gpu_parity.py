@@ -393,3 +393,15 @@ def test_full_layer_bsz8_max_ids(torch_dev, v3_layer):
     say("full layer bsz 8 (64 ids)")
     x, ids, w, got = run_layer_case(torch, lay, ox, 3, 200, 8)
     check_close(got, oracle.moe_layer(ox, x, ids, w, E3), "layer bsz8")
+
+
+def test_read_probe_runs(torch_dev):
+    """The calibration read touches only its buffer and leaves the sink alone."""
+    torch = torch_dev
+    say("read probe")
+    buf = torch.ones(1 << 22, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for nb in (1024, 5 * 1024, 1 << 22):
+        dm.read_probe(buf, nb, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
