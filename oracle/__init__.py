@@ -21,9 +21,12 @@ Sources, cited by page title and section:
   - section "先用 Qwen3 练级，再让 Qwen3.5 充当高压试炼场" (sub-128 TP slices,
     multiple_of 64/32);
   - section "16 tok/s 之后：一段没有跑通的路" (MoE forward breakdown block:
-    per-box partials, host reduce).
+    per-box partials, host reduce);
+  - the memory section above and the Qwen3 section (fp8 checkpoints with a
+    128 x 128 block-scale format; converted to fp9 by ``fp8.py``).
 * chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2 "两条路线的判断"
-  (route one: bsz=2, top_k=8 routed experts per token, near-disjoint sets).
+  (route one: bsz=2, top_k=8 routed experts per token, near-disjoint sets);
+  section 9.5 (the GPU stage normalises between layers: the stack glue).
 * ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
   "形态一：Mac-to-Mac 张量并行（RDMA）" (TP partial sums are f32).
 
@@ -37,9 +40,16 @@ from .fp9 import (  # noqa: F401
     FP9_MAX,
     decode,
     quantize,
+    quantize_f64,
     pack,
     unpack,
     decode_planes,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    decode_e4m3,
+    dequantize,
+    fp8_to_fp9,
 )
 from .moe import (  # noqa: F401
     gemv,

@@ -78,8 +78,26 @@ def quantize(x):
     xf = np.asarray(x, dtype=np.float32)
     if np.any(np.isnan(xf)):
         raise ValueError("fp9 quantize: NaN input")
-    a = np.abs(xf.astype(np.float64))
-    neg = np.signbit(xf)
+    return _quantize_f64(xf.astype(np.float64), np.signbit(xf))
+
+
+def quantize_f64(x):
+    """float64 values -> 9-bit codes with the same rounding as `quantize`.
+
+    For values that are not float32 numbers (such as an fp8 value times a
+    block scale, computed exactly): one rounding from the exact value, where
+    rounding to float32 first could round twice.  For float32 inputs it equals
+    `quantize`.
+    """
+    xd = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(xd)):
+        raise ValueError("fp9 quantize: NaN input")
+    return _quantize_f64(xd, np.signbit(xd))
+
+
+def _quantize_f64(xd, neg):
+    """Steps 2..5 of `quantize` on exact float64 values xd with sign bits neg."""
+    a = np.abs(xd)
 
     mag = np.zeros(a.shape, dtype=np.int64)
 
