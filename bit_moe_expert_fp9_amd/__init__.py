@@ -15,6 +15,7 @@ from .duckmoe import (  # noqa: F401
     Stack,
     decode_fp9,
     expert_ffn,
+    fp8_to_fp9_device,
     gemv_fp9,
     lib,
     moe_down,

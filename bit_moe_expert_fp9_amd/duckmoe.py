@@ -61,6 +61,7 @@ _SIGNATURES = {
     "duckmoe_decode_fp9": ([_P, _P, _I64, _P, _P], ctypes.c_int),
     "duckmoe_gemv_fp9": ([_P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "duckmoe_moe_plan": ([_P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "duckmoe_fp8_to_fp9": ([_P, _P, _I64, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
     "duckmoe_read_probe": ([_P, _SZ, _P, _P], ctypes.c_int),
     "duckmoe_quantize_fp9_device": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "duckmoe_rms_normalize": ([_P, _I32, _I32, ctypes.c_float, _P, _P], ctypes.c_int),
@@ -165,6 +166,29 @@ def quantize_fp9_device(w, body=None, sign=None, nonfinite=None, stream=None):
     return body, sign
 
 
+def fp8_to_fp9_device(codes, scale, block=128, body=None, sign=None, nonfinite=None,
+                      stream=None):
+    """Device E4M3 codes [rows, cols] (uint8) with float32 block scales
+    [ceil(rows/block), ceil(cols/block)] -> (body, sign) fp9 planes on the GPU."""
+    import torch
+    _need_device(codes, torch.uint8, "codes")
+    _need_device(scale, torch.float32, "scale")
+    rows, cols = codes.shape
+    nb = (-(-rows // block), -(-cols // block))
+    if tuple(scale.shape) != nb:
+        raise ValueError("scale grid must be %s" % (nb,))
+    if body is None:
+        body = torch.empty((rows, cols), dtype=torch.uint8, device=codes.device)
+    if sign is None:
+        sign = torch.empty((rows, max(cols // 8, 0)), dtype=torch.uint8, device=codes.device)
+    if body.numel() < rows * cols or sign.numel() < rows * (cols // 8):
+        raise ValueError("body/sign too small")
+    _check(lib().duckmoe_fp8_to_fp9(_ptr(codes), _ptr(scale), rows, cols, block, _ptr(body),
+                                    _ptr(sign), _ptr(nonfinite), _stream(stream)),
+           "duckmoe_fp8_to_fp9")
+    return body, sign
+
+
 # ----------------------------------------------------------------- layer ----
 
 class Layer:
@@ -213,6 +237,19 @@ class Layer:
                                        self.gu_sign[(e * 2 + 1) * mat // 8:]),
                                       (down, H, self.dn_body[e * mat:], self.dn_sign[e * mat // 8:])):
             quantize_fp9_device(src, body=body, sign=sign, nonfinite=nonfinite, stream=stream)
+
+    def set_expert_fp8(self, e, gate, up, down, block=128, nonfinite=None, stream=None):
+        """Convert fp8 matrices into expert e on the GPU.  gate, up, down are
+        (codes uint8, scale float32) device pairs: gate/up codes [I, H], down
+        [H, I], scales on 128 x 128 blocks (see duckmoe_fp8_to_fp9)."""
+        H, I = self.hidden, self.inter
+        mat = I * H
+        for (codes, sc), body, sign in ((gate, self.gu_body[e * 2 * mat:], self.gu_sign[e * 2 * mat // 8:]),
+                                        (up, self.gu_body[(e * 2 + 1) * mat:],
+                                         self.gu_sign[(e * 2 + 1) * mat // 8:]),
+                                        (down, self.dn_body[e * mat:], self.dn_sign[e * mat // 8:])):
+            fp8_to_fp9_device(codes, sc, block, body=body, sign=sign, nonfinite=nonfinite,
+                              stream=stream)
 
     def fill_synthetic_device(self, seed, workload, layer):
         """Draw every expert with synth.weights_device and quantize it on the GPU."""

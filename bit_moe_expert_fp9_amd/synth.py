@@ -58,6 +58,20 @@ def weights_device(seed, workload, layer, expert, matrix, shape, device="cuda"):
     return out
 
 
+def fp8_weights(seed, workload, layer, expert, matrix, shape, block=128):
+    """Synthetic fp8 checkpoint matrix: (codes uint8 [rows, cols], scales float32
+    [ceil(rows/block), ceil(cols/block)]).  Codes are uniform over the 254
+    non-NaN E4M3 codes (every exponent, both signs); scales are 10^U(-5, -3)
+    per block.  Bytes and scales are drawn, nothing is rounded here."""
+    rng = _rng(seed, workload, layer, expert, matrix, 4)
+    rows, cols = shape
+    codes = rng.integers(0, 254, size=shape, dtype=np.int64)
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)  # skip 0x7F and 0xFF
+    nb = (-(-rows // block), -(-cols // block))
+    scales = (10.0 ** rng.uniform(-5.0, -3.0, size=nb)).astype(np.float32)
+    return codes, scales
+
+
 def activations(seed, workload, layer, step, T, hidden):
     """x [T, hidden] ~ N(0, 1), float32."""
     rng = _rng(seed, workload, layer, step, 1)

@@ -18,6 +18,9 @@
  *  [route] chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2
  *          "两条路线的判断": 8 routed experts per token (top_k = 8); the sets of
  *          two tokens barely overlap, so bsz 2 reads about twice the weights.
+ *  [fp8]   same page, sections "真正埋下伏笔的是内存；R1 之后，问题第一次被改写"
+ *          (the released checkpoints are fp8) and "先用 Qwen3 练级，再让
+ *          Qwen3.5 充当高压试炼场" (the fp8 format uses 128 x 128 block scales).
  *  [lane]  chapter page "第 9 章 MTP1 dual-lane overlap", section 9.5
  *          "pair runtime：stage0/stage1 调度": per decoder layer, a GPU stage
  *          (attention, layernorm, residual add) precedes the FFN/MoE stage,
@@ -120,6 +123,26 @@ int duckmoe_quantize_fp9(const float *w, int64_t rows, int64_t cols,
 int duckmoe_quantize_fp9_device(const float *w, int64_t rows, int64_t cols,
                                 uint8_t *body, uint8_t *sign, int32_t *nonfinite,
                                 hipStream_t stream);
+
+/*
+ * [fp8][fp9] Convert an fp8 weight matrix with block scales to fp9 planes on
+ * the GPU, asynchronous on `stream`; all pointers DEVICE.
+ *   fp8   [rows][cols] uint8, finite-only E4M3 codes (exponent bias 7,
+ *         subnormals, no infinities, NaN = 0x7F/0xFF), 8-byte aligned
+ *   scale [ceil(rows/block)][ceil(cols/block)] float32, row-major, 4-byte aligned;
+ *         element (r, c) has weight value(code) * scale[r/block][c/block]
+ *   body  [rows][cols] uint8 (8-byte aligned), sign [rows][cols/8] uint8:
+ *         the fp9 planes, rounded once from the exact product (nearest, ties to
+ *         even, saturating at +-61440: the quantizer's rounding)
+ *   nonfinite: device int32 or NULL; set to 1 if a code is NaN or a product is
+ *         NaN (never cleared by the call)
+ * Errors (host-side): DUCKMOE_EINVAL for negative sizes, block < 8, null or
+ * misaligned pointers; DUCKMOE_ESHAPE if cols or block is not a multiple of 8.
+ * rows or cols == 0 is a no-op.
+ */
+int duckmoe_fp8_to_fp9(const uint8_t *fp8, const float *scale, int64_t rows, int64_t cols,
+                       int32_t block, uint8_t *body, uint8_t *sign, int32_t *nonfinite,
+                       hipStream_t stream);
 
 /*
  * Bytes of device workspace duckmoe_expert_ffn / duckmoe_moe_layer need for T

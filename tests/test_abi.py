@@ -154,6 +154,22 @@ def test_device_quantizer_and_glue_errors(L):
     assert r(FAKE, 0, 16, 0.0, FAKE, None) == 0
 
 
+def test_fp8_converter_errors(L):
+    E = dm.duckmoe
+    f = lambda fp8=FAKE, sc=FAKE, r=2, c=8, b=128, body=FAKE, sign=FAKE: \
+        L.duckmoe_fp8_to_fp9(fp8, sc, r, c, b, body, sign, None, None)
+    assert f(r=-1) == E.EINVAL
+    assert f(b=4) == E.EINVAL
+    assert f(c=12) == E.ESHAPE
+    assert f(b=100) == E.ESHAPE
+    assert f(fp8=None) == E.EINVAL
+    assert f(sc=None) == E.EINVAL
+    assert f(fp8=FAKE + 4) == E.EINVAL
+    assert f(body=FAKE + 4) == E.EINVAL
+    assert f(sc=FAKE + 2) == E.EINVAL
+    assert f(r=0, fp8=None, sc=None, body=None, sign=None) == 0
+
+
 def test_read_probe_errors(L):
     E = dm.duckmoe
     assert L.duckmoe_read_probe(None, 1024, FAKE, None) == E.EINVAL
