@@ -64,6 +64,8 @@ def parse():
                    help="also time the 16-layer stack (about 204 GB of fp9 weights drawn on the "
                         "device) at bsz 1, 2, 4 and 8; results go under 'stack'")
     p.add_argument("--stack-steps", type=int, default=100)
+    p.add_argument("--dense", type=int, default=1,
+                   help="also time the dense fp9 MLP 7168/18432 at bsz 1 and 2 (0 to skip)")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="first run 3 plain device copies of this many MiB (a known-size "
                         "reference for HBM byte counters under rocprofv3 --pmc)")
@@ -217,6 +219,40 @@ def read_ceiling(torch, dm, sizes, reps=100):
     return out
 
 
+DENSE_I, DENSE_WORKLOAD = 18432, 6
+
+
+def time_dense(torch, dm, steps, warmup):
+    """Dense fp9 MLP 7168/18432 (DeepSeek-V3's dense FFN shape) at bsz 1 and 2."""
+    from bit_moe_expert_fp9_amd import synth
+    mlp = dm.Layer(H, DENSE_I, 0, 1).fill_synthetic_device(SEED, DENSE_WORKLOAD, 0)
+    stream = torch.cuda.current_stream()
+    res = {"shape": "7168/18432 SwiGLU MLP, fp9 planes (3 x 7168 x 18432 x 9/8 B)",
+           "weight_bytes": mlp.expert_bytes()}
+    for T in (1, 2):
+        X = torch.from_numpy(np.stack([synth.activations(SEED, DENSE_WORKLOAD, 0, s, T, H)
+                                       for s in range(8)])).cuda()
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        ws = mlp.workspace(T)
+        for s in range(warmup):
+            dm.expert_ffn(mlp, 0, X[s % 8], out=out, ws=ws, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(steps):
+            dm.expert_ffn(mlp, 0, X[s % 8], out=out, ws=ws, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        gbps = mlp.expert_bytes() / (us * 1e-6) / 1e9
+        res["bsz%d" % T] = {"us": us, "tokens_per_s": T / (us * 1e-6), "hbm_gbps": gbps,
+                            "hbm_frac": gbps / HBM_PEAK_GBPS}
+        log("dense bsz%d:" % T, json.dumps(res["bsz%d" % T]))
+    del mlp
+    torch.cuda.empty_cache()
+    return res
+
+
 STACK_LAYERS, STACK_WORKLOAD = 16, 5
 
 
@@ -345,6 +381,8 @@ def main():
     st1 = time_stages(torch, dm, layer, 1, args.steps, args.warmup, draws)
     log("bsz1 stages:", json.dumps(st1))
 
+    dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
+
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
     ceil = read_ceiling(torch, dm, [int(r1["bytes_step"]), int(st1["gate_up_bytes"])])
     (lay_b, (lay_us, lay_gbps)), (gu_b, (gu_us, gu_gbps)) = sorted(ceil.items(), reverse=True)
@@ -379,6 +417,7 @@ def main():
                              "layer_bytes": lay_b, "layer_us": lay_us, "layer_gbps": lay_gbps,
                              "gate_up_bytes": gu_b, "gate_up_us": gu_us, "gate_up_gbps": gu_gbps},
             "layer_frac_of_read_ceiling": gbps / lay_gbps,
+            "dense_mlp": dense,
             "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {

@@ -48,6 +48,7 @@ namespace {
 constexpr int kMaxT = DUCKMOE_MAX_TOKENS;
 constexpr int kMaxIds = DUCKMOE_MAX_IDS;
 constexpr int kChunk = 1024;          // weights per wave-row step: 64 lanes x 16
+constexpr int kMaxInter = 32768;      // intermediate size limit (dense MLPs up to 32 chunks)
 constexpr size_t kHdrBytes = 1024;    // workspace header (status word, plan)
 
 // Launch shape of the gate/up kernel (compile-time; defaults measured on MI355X).
@@ -549,19 +550,30 @@ __device__ __forceinline__ int plan_at(const int32_t *plan, int s) {
   return __builtin_amdgcn_readfirstlane(plan[1 + s]);
 }
 
+// Item q of a block is (slot q / nc, chunk q % nc).  Wave w streams the items
+// q = w, w + WB, ... < nq: the first is already in flight in b0; items
+// alternate between b0 and b1, the next always issued before the current one
+// is computed.  When WB is a multiple of nc every item of a wave has chunk
+// w % nc (the shard combine relies on it).
 template <int T, int R>
+__device__ __forceinline__ void dn_item(DnTile<T, R> &b, const LayerArgs &a, const int32_t *plan,
+                                        __amdgpu_buffer_rsrc_t rh, int q, int nc, int row0,
+                                        int lane) {
+  const int slot = q / nc;
+  const uint32_t k = (uint32_t)(q - slot * nc) * kChunk + lane * 16;
+  dn_issue<T, R>(b, a, plan_at(plan, slot), rh, slot, row0, k, k < (uint32_t)a.I);
+}
+
+template <int T, int R, int WB>
 __device__ __forceinline__ void dn_block(DnTile<T, R> &b0, DnTile<T, R> &b1, const LayerArgs &a,
                                          const int32_t *plan, __amdgpu_buffer_rsrc_t rh,
-                                         int blk, int s0, int per_c, int n_it, uint32_t k,
-                                         bool kv, float (&acc)[R][T][2]) {
-  for (int i = 0; i < n_it; i += 2) {
-    const int slot = s0 + i * per_c;
-    if (i + 1 < n_it)
-      dn_issue<T, R>(b1, a, plan_at(plan, slot + per_c), rh, slot + per_c, blk * R, k, kv);
+                                         int blk, int w, int nq, int nc, int lane,
+                                         float (&acc)[R][T][2]) {
+  for (int q = w; q < nq; q += 2 * WB) {
+    if (q + WB < nq) dn_item<T, R>(b1, a, plan, rh, q + WB, nc, blk * R, lane);
     dn_consume<T, R>(b0, acc);
-    if (i + 1 >= n_it) break;
-    if (i + 2 < n_it)
-      dn_issue<T, R>(b0, a, plan_at(plan, slot + 2 * per_c), rh, slot + 2 * per_c, blk * R, k, kv);
+    if (q + WB >= nq) break;
+    if (q + 2 * WB < nq) dn_item<T, R>(b0, a, plan, rh, q + 2 * WB, nc, blk * R, lane);
     dn_consume<T, R>(b1, acc);
   }
 }
@@ -576,29 +588,24 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nc = (I + kChunk - 1) / kChunk;
-  const int per_c = WB / nc;  // waves per chunk
   const int nblk = (H + R - 1) / R;
-  const int c = wave % nc;
-  const uint32_t k = (uint32_t)c * kChunk + lane * 16;
-  const bool kv = k < (uint32_t)I;
-  const int s0 = wave / nc;  // first slot of this wave in every block
-  const bool active = wave < nc * per_c;
   // h' of every slot the workspace can hold; slots >= n_slots are never read
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hbuf, (uint32_t)(max_slots * a.T * I) * 4u);
   const int ns = a.n_shards;
   const int width = I / ns;
 
-  // A wave whose first item is slot 0 (its expert is known without the plan)
-  // issues it before the plan arrives.
+  // A wave whose first item is in slot 0 (its expert is known without the
+  // plan) issues it before the plan arrives.
   DnTile<T, R> b0, b1;
-  const bool first_now = active && s0 == 0 && (int)blockIdx.x < nblk;
-  if (first_now) dn_issue<T, R>(b0, a, slot0_expert(a), rh, 0, blockIdx.x * R, k, kv);
-  const int S = __builtin_amdgcn_readfirstlane(plan[0]);
-  // items per block for this wave (0 for waves beyond nc * per_c)
-  const int n_it = (active && s0 < S) ? (S - s0 + per_c - 1) / per_c : 0;
-  if (!first_now && n_it > 0 && (int)blockIdx.x < nblk)
-    dn_issue<T, R>(b0, a, plan_at(plan, s0), rh, s0, blockIdx.x * R, k, kv);
+  const bool first_now = wave < nc && (int)blockIdx.x < nblk;
+  if (first_now) {
+    const uint32_t k = (uint32_t)wave * kChunk + lane * 16;
+    dn_issue<T, R>(b0, a, slot0_expert(a), rh, 0, blockIdx.x * R, k, k < (uint32_t)I);
+  }
+  const int nq = __builtin_amdgcn_readfirstlane(plan[0]) * nc;  // items per block
+  if (!first_now && wave < nq && (int)blockIdx.x < nblk)
+    dn_item<T, R>(b0, a, plan, rh, wave, nc, blockIdx.x * R, lane);
 
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     float acc[R][T][2];
@@ -607,11 +614,11 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 #pragma unroll
       for (int t = 0; t < T; ++t) acc[r][t][0] = acc[r][t][1] = 0.0f;
 
-    if (n_it > 0) {
-      dn_block<T, R>(b0, b1, a, plan, rh, blk, s0, per_c, n_it, k, kv, acc);
+    if (wave < nq) {
+      dn_block<T, R, WB>(b0, b1, a, plan, rh, blk, wave, nq, nc, lane, acc);
       // the next block's first item loads while this block is reduced
       if (blk + (int)gridDim.x < nblk)
-        dn_issue<T, R>(b0, a, plan_at(plan, s0), rh, s0, (blk + gridDim.x) * R, k, kv);
+        dn_item<T, R>(b0, a, plan, rh, wave, nc, (blk + gridDim.x) * R, lane);
     }
 
     // lane groups of G lanes -> 64/G partial sums per (wave, row, token)
@@ -648,10 +655,11 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
         c_lo = (shard * width) / kChunk; c_hi = c_lo + 1;
         grp = ((shard * width) % kChunk) / (G * 16);
       }
+      // with n_shards > 1, WB is a multiple of nc and wave w holds chunk w % nc
       float sum = 0.0f;
-      for (int w = 0; w < nc * per_c; ++w) {
+      for (int w = 0; w < WB; ++w) {
         const int cw = w % nc;
-        if (cw >= c_lo && cw < c_hi) sum += red[((w * R + r) * T + t) * 16 + grp];
+        if (ns == 1 || (cw >= c_lo && cw < c_hi)) sum += red[((w * R + r) * T + t) * 16 + grp];
       }
       a.out[((size_t)shard * T + t) * H + row] = sum;
     }
@@ -782,8 +790,9 @@ int gu_tokens_per_pass(int H) {
 
 int check_layer(const duckmoe_layer *L) {
   if (!L || !L->gu_body || !L->gu_sign || !L->dn_body || !L->dn_sign) return DUCKMOE_EINVAL;
-  if (L->hidden < 16 || L->hidden % 16 || L->inter < 16 || L->inter % 16 || L->inter > 4096 ||
-      L->top_k < 1 || L->n_routed < 1 || L->n_routed > DUCKMOE_MAX_ROUTED)
+  if (L->hidden < 16 || L->hidden % 16 || L->inter < 16 || L->inter % 16 ||
+      L->inter > kMaxInter || L->top_k < 1 || L->n_routed < 0 ||
+      L->n_routed > DUCKMOE_MAX_ROUTED)
     return DUCKMOE_ESHAPE;
   // one buffer descriptor spans an expert's gate+up bodies: 2*H*I < 2^31
   if (2ll * L->hidden * L->inter > 0x7fffffffll) return DUCKMOE_ESHAPE;
@@ -794,9 +803,24 @@ int check_layer(const duckmoe_layer *L) {
   return DUCKMOE_OK;
 }
 
+// Launch shape of the down kernel (compile-time; defaults measured on MI355X).
+#ifndef DUCKMOE_DN_WAVES
+#define DUCKMOE_DN_WAVES 2          // waves per workgroup
+#endif
+#ifndef DUCKMOE_DN_ROWS
+#define DUCKMOE_DN_ROWS 7           // output rows per block at T = 1 (see down_rows)
+#endif
+#ifndef DUCKMOE_DN_WAVES_PER_CU
+#define DUCKMOE_DN_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+constexpr int kWB = DUCKMOE_DN_WAVES;
+
 int check_shards(int I, int ns) {
   if (ns < 1 || I % ns) return DUCKMOE_ESHAPE;
   if (ns == 1) return DUCKMOE_OK;
+  // shard partials need every down wave on one 1024-wide chunk
+  const int nc = (I + kChunk - 1) / kChunk;
+  if (kWB % nc) return DUCKMOE_ESHAPE;
   const int w = I / ns;
   if (w % kChunk == 0) return DUCKMOE_OK;
   if (w >= 64 && w <= kChunk && (w & (w - 1)) == 0) return DUCKMOE_OK;
@@ -821,18 +845,6 @@ size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
 size_t ws_need(const duckmoe_layer *L, int T, bool single) {
   return kHdrBytes + hbuf_bytes(L, T, single);
 }
-
-// Launch shape of the down kernel (compile-time; defaults measured on MI355X).
-#ifndef DUCKMOE_DN_WAVES
-#define DUCKMOE_DN_WAVES 2          // waves per workgroup
-#endif
-#ifndef DUCKMOE_DN_ROWS
-#define DUCKMOE_DN_ROWS 7           // output rows per block at T = 1 (see down_rows)
-#endif
-#ifndef DUCKMOE_DN_WAVES_PER_CU
-#define DUCKMOE_DN_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
-#endif
-constexpr int kWB = DUCKMOE_DN_WAVES;
 
 // rows per down block: more rows share each h' load, fewer keep registers in check
 template <int T>

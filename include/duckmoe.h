@@ -75,8 +75,11 @@ extern "C" {
  *                                            element 8j+i in bit i
  *   dn_body [n_routed+1][H][I]       uint8  down rows
  *   dn_sign [n_routed+1][H][I/8]     uint8
- * Requirements: H and I multiples of 16, 16 <= I <= 4096, H >= 16,
- * 1 <= top_k, 1 <= n_routed <= DUCKMOE_MAX_ROUTED (DUCKMOE_ESHAPE otherwise);
+ * Requirements: H and I multiples of 16, 16 <= I <= 32768, H >= 16,
+ * 2 * H * I < 2^31, 1 <= top_k, 0 <= n_routed <= DUCKMOE_MAX_ROUTED
+ * (DUCKMOE_ESHAPE otherwise).  n_routed = 0 describes a dense MLP: its only
+ * expert is index 0, run with duckmoe_expert_ffn (the pages' first fp9
+ * workload was a dense MLP, [fp9]);
  * body pointers 16-byte aligned, sign pointers 2-byte aligned (DUCKMOE_EINVAL).
  * The struct itself is read on the host during the call only.
  */
@@ -168,9 +171,10 @@ size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shar
  *                       the intermediate slice [r*I/n_shards, (r+1)*I/n_shards)
  *                       of every expert ([tp][f32]); the shards add up to the
  *                       n_shards == 1 output.
- *   n_shards >= 1 must divide I, and the slice width I / n_shards must be a
- *   multiple of 1024 or a power of two in [64, 1024] (DUCKMOE_ESHAPE otherwise);
- *   for I = 2048 that is n_shards in {1, 2, 4, 8, 16, 32}.
+ *   n_shards >= 1 must divide I, the slice width I / n_shards must be a
+ *   multiple of 1024 or a power of two in [64, 1024], and n_shards > 1 needs
+ *   I <= 2048 (DUCKMOE_ESHAPE otherwise); for I = 2048 that is n_shards in
+ *   {1, 2, 4, 8, 16, 32}.
  *   ws  device workspace, 256-byte aligned, >= duckmoe_workspace_bytes(L,T,n_shards)
  * Ids outside [0, n_routed) are skipped and flag DUCKMOE_STATUS_BAD_ID; an id
  * repeated within a token has its weights added and flags DUCKMOE_STATUS_DUP_ID.

@@ -73,6 +73,11 @@ def test_workspace_bytes(L):
     assert f(ctypes.byref(lay), 9, 1) == 0
     assert f(ctypes.byref(lay), 1, 3) == 0      # 2048 / 3 not integral
     assert f(ctypes.byref(lay), 1, 64) == 0     # slice of 32 < 64
+    wide = fake_layer(I=3072)                    # 3 chunks of 1024: no shard partials
+    assert f(ctypes.byref(wide), 1, 1) == 1024 + 9 * 3072 * 4
+    assert f(ctypes.byref(wide), 1, 3) == 0
+    dense = fake_layer(I=18432, E=0, k=1)        # a dense MLP: one expert, index 0
+    assert f(ctypes.byref(dense), 1, 1) == 1024 + 2 * 18432 * 4
     assert f(None, 1, 1) == 0
 
 
@@ -102,8 +107,8 @@ def test_layer_argument_errors(L, fn):
     assert c(ws_bytes=1000) == E.EWORKSPACE
     big = fake_layer(k=40)
     assert call_layer(L, big, T=2, fn=fn) == E.ESHAPE   # T * top_k > 64
-    for bad in (fake_layer(H=7160), fake_layer(I=2040), fake_layer(I=8192), fake_layer(E=0),
-                fake_layer(E=9000), fake_layer(k=0)):
+    for bad in (fake_layer(H=7160), fake_layer(I=2040), fake_layer(I=32784), fake_layer(E=-1),
+                fake_layer(E=9000), fake_layer(k=0), fake_layer(H=65536, I=16384)):
         assert call_layer(L, bad, fn=fn) == E.ESHAPE
     mis = LayerStruct(7168, 2048, 256, 8, FAKE + 8, FAKE, FAKE, FAKE)
     assert call_layer(L, mis, fn=fn) == E.EINVAL
