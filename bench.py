@@ -219,6 +219,56 @@ def read_ceiling(torch, dm, sizes, reps=100):
     return out
 
 
+def time_pair(torch, dm, layer, steps, warmup, draws):
+    """Two tokens per step, three ways: one bsz-2 call, two lanes on their own
+    streams (duckmoe_lane_begin/finish), and two bsz-1 calls in turn."""
+    from bit_moe_expert_fp9_amd import synth
+    n = steps + warmup
+    X = torch.from_numpy(np.stack([synth.activations(SEED, WORKLOAD, 0, 50_000 + s % draws, 2, H)
+                                   for s in range(n)])).cuda()
+    r = [synth.routing(SEED, WORKLOAD, 0, 50_000 + s % draws, 2, E, K) for s in range(n)]
+    IDS = torch.from_numpy(np.stack([a for a, _ in r])).cuda()
+    W = torch.from_numpy(np.stack([b for _, b in r])).cuda()
+    stream = torch.cuda.current_stream()
+    out2 = torch.empty((2, H), dtype=torch.float32, device="cuda")
+    outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    ws1, ws2 = layer.workspace(1), layer.workspace(2)
+    lanes = [dm.Lane(layer), dm.Lane(layer)]
+
+    def bsz2(s):
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=out2, ws=ws2, stream=stream)
+
+    def lanes2(s):
+        for t in range(2):
+            lanes[t].begin(layer, X[s][t:t + 1], IDS[s][t:t + 1], W[s][t:t + 1], outs[t],
+                           producer=stream)
+        for lane in lanes:
+            lane.finish(consumer=stream)
+
+    def serial(s):
+        for t in range(2):
+            dm.moe_layer(layer, X[s][t:t + 1], IDS[s][t:t + 1], W[s][t:t + 1], out=outs[t],
+                         ws=ws1, stream=stream)
+
+    res = {}
+    for name, fn in (("bsz2_call", bsz2), ("two_lanes", lanes2), ("two_serial_calls", serial)):
+        for s in range(warmup):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k in range(steps):
+            fn(warmup + k)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        res[name] = {"us_per_pair": us, "tokens_per_s": 2 / (us * 1e-6)}
+    for lane in lanes:
+        lane.close()
+    log("pair:", json.dumps(res))
+    return res
+
+
 DENSE_I, DENSE_WORKLOAD = 18432, 6
 
 
@@ -382,6 +432,7 @@ def main():
     log("bsz1 stages:", json.dumps(st1))
 
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
+    pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
 
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
     ceil = read_ceiling(torch, dm, [int(r1["bytes_step"]), int(st1["gate_up_bytes"])])
@@ -418,6 +469,7 @@ def main():
                              "gate_up_bytes": gu_b, "gate_up_us": gu_us, "gate_up_gbps": gu_gbps},
             "layer_frac_of_read_ceiling": gbps / lay_gbps,
             "dense_mlp": dense,
+            "pair_two_tokens": pair,
             "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {

@@ -10,6 +10,7 @@ from .duckmoe import (  # noqa: F401
     DuckMoeError,
     EXPORTS,
     LIB_PATH,
+    Lane,
     Layer,
     LayerStruct,
     Stack,

@@ -1098,6 +1098,49 @@ int duckmoe_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_
   return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
 }
 
+int duckmoe_lane_init(duckmoe_lane *lane) {
+  if (!lane) return DUCKMOE_EINVAL;
+  lane->ready = nullptr;
+  lane->done = nullptr;
+  if (hipEventCreateWithFlags(&lane->ready, hipEventDisableTiming) != hipSuccess)
+    return DUCKMOE_EHIP;
+  if (hipEventCreateWithFlags(&lane->done, hipEventDisableTiming) != hipSuccess) {
+    hipEventDestroy(lane->ready);
+    lane->ready = nullptr;
+    return DUCKMOE_EHIP;
+  }
+  return DUCKMOE_OK;
+}
+
+int duckmoe_lane_destroy(duckmoe_lane *lane) {
+  if (!lane) return DUCKMOE_EINVAL;
+  int rc = DUCKMOE_OK;
+  if (lane->ready && hipEventDestroy(lane->ready) != hipSuccess) rc = DUCKMOE_EHIP;
+  if (lane->done && hipEventDestroy(lane->done) != hipSuccess) rc = DUCKMOE_EHIP;
+  lane->ready = lane->done = nullptr;
+  return rc;
+}
+
+int duckmoe_lane_begin(duckmoe_lane *lane, const duckmoe_layer *L, const float *x,
+                       const int32_t *ids, const float *w, int32_t T, float *out,
+                       hipStream_t producer) {
+  if (!lane || !lane->ready || !lane->done || !ids) return DUCKMOE_EINVAL;
+  // argument checks first: nothing is recorded for a call that would fail
+  int rc = run_layer(L, x, ids, w, 0, T, out, 1, lane->ws, lane->ws_bytes, lane->stream, 0);
+  if (rc) return rc;
+  if (hipEventRecord(lane->ready, producer) != hipSuccess) return DUCKMOE_EHIP;
+  if (hipStreamWaitEvent(lane->stream, lane->ready, 0) != hipSuccess) return DUCKMOE_EHIP;
+  rc = run_layer(L, x, ids, w, 0, T, out, 1, lane->ws, lane->ws_bytes, lane->stream, kBoth);
+  if (rc) return rc;
+  return hipEventRecord(lane->done, lane->stream) == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+int duckmoe_lane_finish(duckmoe_lane *lane, hipStream_t consumer) {
+  if (!lane || !lane->done) return DUCKMOE_EINVAL;
+  if (!consumer) return hipEventSynchronize(lane->done) == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+  return hipStreamWaitEvent(consumer, lane->done, 0) == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
 int duckmoe_status(const void *ws, int32_t *status, hipStream_t stream) {
   if (!ws || !status) return DUCKMOE_EINVAL;
   WsHeader h;

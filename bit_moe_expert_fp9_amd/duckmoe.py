@@ -42,6 +42,16 @@ class LayerStruct(ctypes.Structure):
     ]
 
 
+class LaneStruct(ctypes.Structure):
+    _fields_ = [
+        ("stream", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+        ("ready", ctypes.c_void_p),
+        ("done", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -62,6 +72,11 @@ _SIGNATURES = {
     "duckmoe_gemv_fp9": ([_P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "duckmoe_moe_plan": ([_P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "duckmoe_fp8_to_fp9": ([_P, _P, _I64, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "duckmoe_lane_init": ([ctypes.POINTER(LaneStruct)], ctypes.c_int),
+    "duckmoe_lane_destroy": ([ctypes.POINTER(LaneStruct)], ctypes.c_int),
+    "duckmoe_lane_begin": ([ctypes.POINTER(LaneStruct), ctypes.POINTER(LayerStruct), _P, _P, _P,
+                            _I32, _P, _P], ctypes.c_int),
+    "duckmoe_lane_finish": ([ctypes.POINTER(LaneStruct), _P], ctypes.c_int),
     "duckmoe_read_probe": ([_P, _SZ, _P, _P], ctypes.c_int),
     "duckmoe_quantize_fp9_device": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "duckmoe_rms_normalize": ([_P, _I32, _I32, ctypes.c_float, _P, _P], ctypes.c_int),
@@ -393,6 +408,47 @@ def read_probe(buf, nbytes, sink, stream=None):
     """Plain streaming read of the first nbytes of device tensor buf (calibration)."""
     _check(lib().duckmoe_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
            "duckmoe_read_probe")
+
+
+class Lane:
+    """An asynchronous lane: its own stream (default priority), workspace and
+    events (see duckmoe_lane_* in the header)."""
+
+    def __init__(self, layer, max_tokens=1):
+        import torch
+        self.stream = torch.cuda.Stream(device=layer.gu_body.device)
+        self.ws = layer.workspace(max_tokens)
+        self.struct = LaneStruct(self.stream.cuda_stream, self.ws.data_ptr(), self.ws.numel(),
+                                 None, None)
+        _check(lib().duckmoe_lane_init(ctypes.byref(self.struct)), "duckmoe_lane_init")
+
+    def begin(self, layer, x, ids, w, out, producer=None):
+        """Start the layer for this lane once `producer` (default: the current
+        stream) has produced x, ids and w; returns at once."""
+        import torch
+        _need_device(x, torch.float32, "x")
+        _need_device(ids, torch.int32, "ids")
+        _need_device(w, torch.float32, "w")
+        _need_device(out, torch.float32, "out")
+        _check(lib().duckmoe_lane_begin(ctypes.byref(self.struct), ctypes.byref(layer.struct),
+                                        _ptr(x), _ptr(ids), _ptr(w), x.shape[0], _ptr(out),
+                                        _stream(producer)), "duckmoe_lane_begin")
+
+    def finish(self, consumer=None, block=False):
+        """Make `consumer` (default: the current stream) wait for the lane's
+        layer, or block the host if block=True."""
+        c = ctypes.c_void_p(0) if block else _stream(consumer)
+        _check(lib().duckmoe_lane_finish(ctypes.byref(self.struct), c), "duckmoe_lane_finish")
+
+    def close(self):
+        if self.struct.done or self.struct.ready:
+            _check(lib().duckmoe_lane_destroy(ctypes.byref(self.struct)), "duckmoe_lane_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 def status(ws, stream=None):

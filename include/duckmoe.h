@@ -25,6 +25,11 @@
  *          "pair runtime：stage0/stage1 调度": per decoder layer, a GPU stage
  *          (attention, layernorm, residual add) precedes the FFN/MoE stage,
  *          and layer i+1 of a lane waits for layer i's MoE result.
+ *  [pair]  same chapter page, section 9.5: lanes keep separate input and
+ *          output buffers, and one lane's MoE stage is dispatched only after
+ *          an event recorded behind the work that produced its input; section
+ *          9.6 "Rust overlap 接口": begin starts a lane's MoE forward and returns
+ *          at once, finish waits for it and hands over the result.
  *  [f32]   ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
  *          "形态一：Mac-to-Mac 张量并行（RDMA）": TP partial sums travel as f32.
  *
@@ -234,6 +239,40 @@ size_t duckmoe_stack_workspace_bytes(const duckmoe_layer *layers, int32_t n_laye
 int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float *x,
                       const int32_t *ids, const float *w, int32_t T, float eps, float *out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * [pair] Asynchronous lanes.  A lane owns a stream, a workspace and two HIP
+ * events, so two tokens (two lanes) can have their layers in flight at once
+ * while other work runs on the caller's streams.  The struct is caller-owned;
+ * duckmoe_lane_init fills the events (no device memory is allocated) and
+ * duckmoe_lane_destroy releases them.
+ *   stream    the lane's stream (created by the caller, default priority)
+ *   ws        the lane's workspace: >= duckmoe_workspace_bytes(L, T, 1) for the
+ *             largest T it will run, 256-byte aligned; one lane per workspace
+ * duckmoe_lane_begin records an event on `producer` (the stream that wrote x,
+ * ids and w; 0 = the null stream), makes the lane's stream wait for it, runs
+ * duckmoe_moe_layer there and records the lane's done event.  It returns
+ * without waiting.  x, ids, w and out must stay valid until finish.
+ * duckmoe_lane_finish makes `consumer` wait for the done event (no host
+ * blocking); consumer == NULL blocks the host until the lane's layer is done.
+ * Errors: DUCKMOE_EINVAL for a null lane or stream fields, plus the errors of
+ * duckmoe_moe_layer (checked before anything is recorded); DUCKMOE_EHIP if the
+ * runtime refuses an event operation.
+ */
+typedef struct duckmoe_lane {
+  hipStream_t stream;
+  void *ws;
+  size_t ws_bytes;
+  hipEvent_t ready;  /* set by duckmoe_lane_init */
+  hipEvent_t done;   /* set by duckmoe_lane_init */
+} duckmoe_lane;
+
+int duckmoe_lane_init(duckmoe_lane *lane);
+int duckmoe_lane_destroy(duckmoe_lane *lane);
+int duckmoe_lane_begin(duckmoe_lane *lane, const duckmoe_layer *L, const float *x,
+                       const int32_t *ids, const float *w, int32_t T, float *out,
+                       hipStream_t producer);
+int duckmoe_lane_finish(duckmoe_lane *lane, hipStream_t consumer);
 
 /*
  * Reads the status word the last layer call on this workspace wrote

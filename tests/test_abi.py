@@ -175,6 +175,20 @@ def test_fp8_converter_errors(L):
     assert f(r=0, fp8=None, sc=None, body=None, sign=None) == 0
 
 
+def test_lane_errors(L):
+    from bit_moe_expert_fp9_amd.duckmoe import LaneStruct
+    E = dm.duckmoe
+    assert L.duckmoe_lane_init(None) == E.EINVAL
+    assert L.duckmoe_lane_destroy(None) == E.EINVAL
+    assert L.duckmoe_lane_finish(None, None) == E.EINVAL
+    lane = LaneStruct(None, FAKE, 1 << 30, None, None)       # events never created
+    lay = fake_layer()
+    assert L.duckmoe_lane_begin(ctypes.byref(lane), ctypes.byref(lay), FAKE, FAKE, FAKE, 1,
+                                FAKE, None) == E.EINVAL
+    assert L.duckmoe_lane_finish(ctypes.byref(lane), None) == E.EINVAL
+    assert L.duckmoe_lane_destroy(ctypes.byref(lane)) == 0   # nothing to release
+
+
 def test_read_probe_errors(L):
     E = dm.duckmoe
     assert L.duckmoe_read_probe(None, 1024, FAKE, None) == E.EINVAL
