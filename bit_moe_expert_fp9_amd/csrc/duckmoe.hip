@@ -667,6 +667,418 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
   }
 }
 
+// -------------------------------------------------- matrix-core path ----
+// For T >= 3 tokens the FMA count per weight (one per token) makes the vector
+// kernels ALU-bound, so the contractions go to the matrix cores instead:
+// v_mfma_f32_16x16x32_f16 takes a 16 x 32 fp16 A, a 32 x 16 fp16 B and an f32
+// accumulator.  The fp9 weights decode exactly to fp16 (A).  The activations
+// (B) are float32; each is split into two fp16 numbers, hi = fp16(v) and
+// lo = fp16((v - hi) * 2^11), after scaling every token row (x) or (slot,
+// token) row (h') by a power of two that puts its largest magnitude in
+// [2^13, 2^14), so neither part overflows and the pair carries about 22 bits.
+// Two MFMAs (A*hi, A*lo) per step, recombined in f32 as acc_hi + acc_lo * 2^-11
+// and unscaled exactly.
+//
+// Lane layout (checked on gfx950): A[i][k] is in lane i + 16 * (k / 8), element
+// k % 8; B[k][j] in lane j + 16 * (k / 8), element k % 8; the accumulator
+// element D[i][j] in lane j + 16 * (i / 4), element i % 4.  The k index only has
+// to agree between A and B, so lane group g = lane / 16 takes 32 consecutive
+// columns c .. c + 31 of its row (two 16-byte body loads and 4 sign bytes), and
+// step s of a 128-column unit consumes columns c + 8s .. c + 8s + 7.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMxUnit = 128;   // columns per unit: 4 lane groups x 32
+constexpr int kMxGroups = 8;   // slot groups of the down pass (partials per row)
+constexpr float kLoScale = 2048.0f;
+
+struct MxArgs {
+  _Float16 *xh, *xl;  // [T][Hp] scaled activations, hi and lo parts (zero padded)
+  float *xinv;        // [T] 2^-k of each token's scale
+  _Float16 *hh, *hl;  // [slots][T][Ip] scaled h'
+  float *hinv;        // [slots][T]
+  float *part;        // [kMxGroups][T][H] down partials
+  int Hp, Ip;         // H, I rounded up to whole units
+};
+
+// power-of-two scale 2^k with max * 2^k in [2^13, 2^14) (k clamped to +-126)
+__device__ __forceinline__ int mx_scale_exp(float m) {
+  if (!(m > 0.0f)) return 0;
+  int e;
+  frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+  return max(-126, min(126, 14 - e));
+}
+
+__device__ __forceinline__ void mx_split(float v, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)((v - (float)hi) * kLoScale);
+}
+
+// Split one row of n floats (optionally divided by r first) into scaled hi/lo
+// parts of width np (zeros past n); returns 2^-k.  One workgroup of 256 threads.
+__device__ float mx_prep_row(const float *src, int n, int np, float r, _Float16 *hi,
+                             _Float16 *lo, float *red) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(src[i] / r));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const int k = mx_scale_exp(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  const float sc = ldexpf(1.0f, k);
+  for (int i = threadIdx.x; i < np; i += 256) {
+    _Float16 h = (_Float16)0.0f, l = (_Float16)0.0f;
+    if (i < n) mx_split((src[i] / r) * sc, h, l);
+    hi[i] = h;
+    lo[i] = l;
+  }
+  return ldexpf(1.0f, -k);
+}
+
+// One workgroup per token: x (or its RMS-normalized form, the stack glue) ->
+// scaled hi/lo parts.  The glue divides by the same divisor as k_rms.
+__global__ __launch_bounds__(256) void k_mx_xprep(const LayerArgs a, const MxArgs m) {
+  __shared__ float red[4];
+  __shared__ float part[4];
+  const int t = blockIdx.x;
+  const float *row = a.x + (size_t)t * a.H;
+  float r = 1.0f;
+  if (a.in_rms) {
+    const float ss = rms_wave_part(row, a.H);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    r = rms_divisor(part, a.H, a.in_eps);
+  }
+  const float inv = mx_prep_row(row, a.H, m.Hp, r, m.xh + (size_t)t * m.Hp,
+                                m.xl + (size_t)t * m.Hp, red);
+  if (threadIdx.x == 0) m.xinv[t] = inv;
+}
+
+// One workgroup per (slot, token) row of h' (rows of slots past the plan exit).
+__global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArgs m) {
+  __shared__ float red[4];
+  const int32_t *plan = reinterpret_cast<const int32_t *>(
+      reinterpret_cast<const uint8_t *>(a.hdr) + kPlanOff);
+  const int slot = blockIdx.x / a.T, t = blockIdx.x - slot * a.T;
+  if (slot >= __builtin_amdgcn_readfirstlane(plan[0])) return;
+  const size_t rowi = (size_t)slot * a.T + t;
+  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hh + rowi * m.Ip,
+                                m.hl + rowi * m.Ip, red);
+  if (threadIdx.x == 0) m.hinv[rowi] = inv;
+}
+
+struct MxTile {     // one unit of one 16-row block for one lane
+  uint4 b0, b1;     // 32 body bytes: columns c .. c + 31
+  uint32_t s0, s1;  // their sign bits (16 + 16)
+};
+
+__device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
+                                          __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
+                                          uint32_t c, bool rv) {
+  const bool v0 = rv && c < K, v1 = rv && c + 16 < K;
+  w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
+  w.b1 = buf_load16(rb, v1 ? row * K + c + 16 : kOutOfRange);
+  w.s0 = buf_load2(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
+  w.s1 = buf_load2(rs, v1 ? row * (K / 8) + c / 8 + 2 : kOutOfRange);
+}
+
+struct MxAct {      // the lane's 32 activations of one unit, hi and lo
+  uint4 h[4], l[4];
+};
+
+__device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t rh,
+                                          __amdgpu_buffer_rsrc_t rl, uint32_t off, bool v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    b.h[s] = buf_load16(rh, v ? off + 16 * s : kOutOfRange);
+    b.l[s] = buf_load16(rl, v ? off + 16 * s : kOutOfRange);
+  }
+}
+
+// acc_hi += A * B_hi, acc_lo += A * B_lo over the unit's 4 steps
+__device__ __forceinline__ void mx_mma(const MxTile &w, const MxAct &b, f4v_t &ah, f4v_t &al) {
+  h2_t d[16];
+  fp9_decode16(w.b0, w.s0, d);
+  fp9_decode16(w.b1, w.s1, d + 8);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const half8_t A = __builtin_bit_cast(half8_t, make_uint4(
+        __builtin_bit_cast(uint32_t, d[4 * s]), __builtin_bit_cast(uint32_t, d[4 * s + 1]),
+        __builtin_bit_cast(uint32_t, d[4 * s + 2]), __builtin_bit_cast(uint32_t, d[4 * s + 3])));
+    ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, b.h[s]), ah, 0, 0, 0);
+    al = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, b.l[s]), al, 0, 0, 0);
+  }
+}
+
+// A wave's work in the two matrix-core kernels is one flat stream of items:
+// for each task of its workgroup (in order), the units u = wave, wave + WA, ...
+// of the task, or one empty item (u = -1) when the wave has no unit in it, so
+// that every wave closes every task exactly once (the close has a barrier).
+// The loads of the next item, possibly in the next task, are issued before the
+// current one is computed.
+struct MxItem {
+  int task;
+  int u;  // unit index, -1 for the empty item
+};
+
+__device__ __forceinline__ MxItem mx_first(int wave, int nu) {
+  return MxItem{(int)blockIdx.x, wave < nu ? wave : -1};
+}
+
+template <int WA>
+__device__ __forceinline__ MxItem mx_next(MxItem it, int wave, int nu) {
+  if (it.u >= 0 && it.u + WA < nu) return MxItem{it.task, it.u + WA};
+  return MxItem{it.task + (int)gridDim.x, wave < nu ? wave : -1};
+}
+
+template <int WA>
+__device__ __forceinline__ bool mx_last(MxItem it, int nu) {
+  return it.u < 0 || it.u + WA >= nu;
+}
+
+// Gate/up: a workgroup of WA waves takes whole tasks (slot, block of 16 * RT
+// rows) and splits the task's units (128 columns of H) over its waves; the
+// waves' partial accumulators meet in LDS, wave 0 sums them in a fixed order and
+// writes h' = w * silu(gate) * up for the block's rows and every token.
+template <int WA, int RT>
+struct GuMxBuf {
+  MxTile g[RT], u[RT];
+  MxAct b;
+};
+
+template <int WA, int RT>
+__global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const MxArgs m) {
+  __shared__ f4v_t red[2][WA][RT * 4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.H, I = a.I, T = a.T;
+  const int nu = m.Hp / kMxUnit;
+  const int NB = (I + 16 * RT - 1) / (16 * RT);  // row blocks per slot (last may be partial)
+  const PlanIn pin = plan_load(a);
+  const WavePlan plan = wave_plan(a, pin);
+  if (blockIdx.x == 0 && wave == 0) plan_store(plan, a);
+  const int ntask = plan.n_slots * NB;
+  const int j = lane & 15, g = lane >> 4;
+  const uint32_t mat = (uint32_t)I * (uint32_t)H;
+  const __amdgpu_buffer_rsrc_t rxh = make_rsrc(m.xh, (uint32_t)(T * m.Hp) * 2u);
+  const __amdgpu_buffer_rsrc_t rxl = make_rsrc(m.xl, (uint32_t)(T * m.Hp) * 2u);
+  const bool jv = j < T;
+
+  auto issue = [&](GuMxBuf<WA, RT> &bf, MxItem it) {
+    if (it.u < 0) return;
+    const int slot = it.task / NB, r0 = (it.task - slot * NB) * 16 * RT;
+    const int e = plan_expert(plan, slot);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
+    const uint32_t c = (uint32_t)(it.u * kMxUnit + 32 * g);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int row = r0 + 16 * t + j;
+      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c, row < I);
+      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c, row < I);
+    }
+    mx_load_b(bf.b, rxh, rxl, ((uint32_t)j * m.Hp + c) * 2u, jv);
+  };
+
+  f4v_t acc[RT][4];
+  auto zero = [&]() {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[t][f] = f4v_t{0, 0, 0, 0};
+  };
+  zero();
+  int parity = 0;
+
+  auto consume = [&](const GuMxBuf<WA, RT> &bf, MxItem it) {
+    if (it.u >= 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        mx_mma(bf.g[t], bf.b, acc[t][0], acc[t][1]);
+        mx_mma(bf.u[t], bf.b, acc[t][2], acc[t][3]);
+      }
+    }
+    if (!mx_last<WA>(it, nu)) return;
+    // close the task: partials to LDS, wave 0 reduces and writes h'
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) red[parity][wave][4 * t + f][lane] = acc[t][f];
+    zero();
+    __syncthreads();
+    if (wave == 0) {
+      const int slot = it.task / NB, r0 = (it.task - slot * NB) * 16 * RT;
+      float wt = 0.0f;
+      for (int t = 0; t < T; ++t) {
+        const float w_t = plan_weight(plan, a, slot, t);
+        if (t == j) wt = w_t;
+      }
+      const float xs = jv ? m.xinv[j] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        f4v_t G = {0, 0, 0, 0}, Gl = G, U = G, Ul = G;
+#pragma unroll
+        for (int w = 0; w < WA; ++w) {
+          G += red[parity][w][4 * t + 0][lane];
+          Gl += red[parity][w][4 * t + 1][lane];
+          U += red[parity][w][4 * t + 2][lane];
+          Ul += red[parity][w][4 * t + 3][lane];
+        }
+        if (jv) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 16 * t + 4 * g + r;
+            const float gs = (G[r] + Gl[r] * (1.0f / kLoScale)) * xs;
+            const float us = (U[r] + Ul[r] * (1.0f / kLoScale)) * xs;
+            const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gs) * us);
+            if (row < I) a.hbuf[((size_t)slot * T + j) * I + row] = hv;
+          }
+        }
+      }
+    }
+    parity ^= 1;
+  };
+
+  GuMxBuf<WA, RT> b0, b1;
+  MxItem i0 = mx_first(wave, nu), i1;
+  if (i0.task < ntask) issue(b0, i0);
+  while (i0.task < ntask) {
+    i1 = mx_next<WA>(i0, wave, nu);
+    if (i1.task < ntask) issue(b1, i1);
+    consume(b0, i0);
+    if (i1.task >= ntask) break;
+    i0 = mx_next<WA>(i1, wave, nu);
+    if (i0.task < ntask) issue(b0, i0);
+    consume(b1, i1);
+  }
+}
+
+// Down: a workgroup takes tasks (block of 16 * RT rows of H, slot group q) and
+// splits the (slot, unit of I) items of the group's slots over its waves; each
+// item's hi/lo accumulators are unscaled into the wave's running sum; the
+// waves' sums meet in LDS and wave 0 writes the group's partial for the block's
+// rows.  The groups' partials are added by k_mx_reduce in a fixed order.
+template <int WA, int RT>
+struct DnMxBuf {
+  MxTile w[RT];
+  MxAct b;
+  float hs;
+};
+
+template <int WA, int RT>
+__global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const MxArgs m) {
+  __shared__ f4v_t red[2][WA][RT][64];
+  const int32_t *plan = reinterpret_cast<const int32_t *>(
+      reinterpret_cast<const uint8_t *>(a.hdr) + kPlanOff);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.H, I = a.I, T = a.T;
+  const int S = __builtin_amdgcn_readfirstlane(plan[0]);
+  const int nv = m.Ip / kMxUnit;
+  const int NBH = (H + 16 * RT - 1) / (16 * RT);
+  const int ntask = NBH * kMxGroups;
+  const int j = lane & 15, g = lane >> 4;
+  const bool jv = j < T;
+  const uint32_t mat = (uint32_t)I * (uint32_t)H;
+  const int max_slots = a.ids != nullptr ? T * a.top_k + 1 : 1;
+  const __amdgpu_buffer_rsrc_t rhh = make_rsrc(m.hh, (uint32_t)(max_slots * T * m.Ip) * 2u);
+  const __amdgpu_buffer_rsrc_t rhl = make_rsrc(m.hl, (uint32_t)(max_slots * T * m.Ip) * 2u);
+  // items of the task's group: (slot q + s * G, unit v) for s < ns_q, v < nv
+  auto n_items = [&](int task) {
+    const int q = task / NBH;
+    return (S > q ? (S - q + kMxGroups - 1) / kMxGroups : 0) * nv;
+  };
+  // the stream of items as in k_gate_up_mx, with a per-task item count
+  auto first = [&]() {
+    const int t = blockIdx.x;
+    return MxItem{t, (t < ntask && wave < n_items(t)) ? wave : -1};
+  };
+  auto next = [&](MxItem it) {
+    if (it.u >= 0 && it.u + WA < n_items(it.task)) return MxItem{it.task, it.u + WA};
+    const int t = it.task + (int)gridDim.x;
+    return MxItem{t, (t < ntask && wave < n_items(t)) ? wave : -1};
+  };
+
+  auto issue = [&](DnMxBuf<WA, RT> &bf, MxItem it) {
+    if (it.u < 0) return;
+    const int q = it.task / NBH, blk = it.task - q * NBH;
+    const int si = it.u / nv, v = it.u - si * nv;
+    const int slot = q + si * kMxGroups;
+    const int e = __builtin_amdgcn_readfirstlane(plan[1 + slot]);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
+    const uint32_t c = (uint32_t)(v * kMxUnit + 32 * g);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int row = blk * 16 * RT + 16 * t + j;
+      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c, row < H);
+    }
+    mx_load_b(bf.b, rhh, rhl, ((uint32_t)(slot * T + j) * m.Ip + c) * 2u, jv);
+    bf.hs = jv ? m.hinv[slot * T + j] : 0.0f;
+  };
+
+  f4v_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f4v_t{0, 0, 0, 0};
+  int parity = 0;
+
+  auto consume = [&](const DnMxBuf<WA, RT> &bf, MxItem it) {
+    if (it.u >= 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        f4v_t ah = {0, 0, 0, 0}, al = ah;
+        mx_mma(bf.w[t], bf.b, ah, al);
+        acc[t] += (ah + al * (1.0f / kLoScale)) * bf.hs;
+      }
+    }
+    if (it.u >= 0 && it.u + WA < n_items(it.task)) return;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      red[parity][wave][t][lane] = acc[t];
+      acc[t] = f4v_t{0, 0, 0, 0};
+    }
+    __syncthreads();
+    if (wave == 0 && jv) {
+      const int q = it.task / NBH, blk = it.task - q * NBH;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        f4v_t sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < WA; ++w) sum += red[parity][w][t][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int orow = blk * 16 * RT + 16 * t + 4 * g + r;
+          if (orow < H) m.part[((size_t)q * T + j) * H + orow] = sum[r];
+        }
+      }
+    }
+    parity ^= 1;
+  };
+
+  DnMxBuf<WA, RT> b0, b1;
+  MxItem i0 = first(), i1;
+  if (i0.task < ntask) issue(b0, i0);
+  while (i0.task < ntask) {
+    i1 = next(i0);
+    if (i1.task < ntask) issue(b1, i1);
+    consume(b0, i0);
+    if (i1.task >= ntask) break;
+    i0 = next(i1);
+    if (i0.task < ntask) issue(b0, i0);
+    consume(b1, i1);
+  }
+}
+
+// out[t][row] = the kMxGroups partials added in group order.
+__global__ __launch_bounds__(256) void k_mx_reduce(const LayerArgs a, const MxArgs m) {
+  const int n = a.T * a.H;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kMxGroups; ++q) s += m.part[(size_t)q * n + i];
+  a.out[i] = s;
+}
+
 // ------------------------------------------------------ building blocks ----
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ body,
                                                 const uint8_t *__restrict__ sign, int64_t n,
@@ -841,9 +1253,54 @@ size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
   return hbuf_slots(L, T, single) * (size_t)T * L->inter * sizeof(float);
 }
 
-// header | h' [slots][T][I]
+// Matrix-core path (T >= kMxMinT, no shard partials): launch shape and the
+// workspace it adds after h'.
+#ifndef DUCKMOE_MX_MIN_T
+#define DUCKMOE_MX_MIN_T 3          // smallest T that takes the matrix-core path
+#endif
+#ifndef DUCKMOE_MX_GU_WAVES
+#define DUCKMOE_MX_GU_WAVES 4       // waves per gate/up workgroup
+#endif
+#ifndef DUCKMOE_MX_DN_WAVES
+#define DUCKMOE_MX_DN_WAVES 4       // waves per down workgroup
+#endif
+#ifndef DUCKMOE_MX_ROW_TILES
+#define DUCKMOE_MX_ROW_TILES 2      // 16-row MFMA tiles per task (they share activation loads)
+#endif
+#ifndef DUCKMOE_MX_WAVES_PER_CU
+#define DUCKMOE_MX_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+
+bool use_mx(int T, int n_shards) { return T >= DUCKMOE_MX_MIN_T && n_shards == 1; }
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+struct MxLayout {
+  size_t xh, xl, xinv, hh, hl, hinv, part, end;
+  int Hp, Ip;
+};
+
+MxLayout mx_layout(const duckmoe_layer *L, int T, bool single, size_t base) {
+  MxLayout m;
+  m.Hp = (L->hidden + kMxUnit - 1) / kMxUnit * kMxUnit;
+  m.Ip = (L->inter + kMxUnit - 1) / kMxUnit * kMxUnit;
+  const size_t slots = hbuf_slots(L, T, single);
+  size_t off = align256(base);
+  m.xh = off;   off = align256(off + (size_t)T * m.Hp * 2);
+  m.xl = off;   off = align256(off + (size_t)T * m.Hp * 2);
+  m.xinv = off; off = align256(off + (size_t)T * 4);
+  m.hh = off;   off = align256(off + slots * T * m.Ip * 2);
+  m.hl = off;   off = align256(off + slots * T * m.Ip * 2);
+  m.hinv = off; off = align256(off + slots * T * 4);
+  m.part = off; off = align256(off + (size_t)kMxGroups * T * L->hidden * 4);
+  m.end = off;
+  return m;
+}
+
+// header | h' [slots][T][I] | (T >= kMxMinT) matrix-core buffers
 size_t ws_need(const duckmoe_layer *L, int T, bool single) {
-  return kHdrBytes + hbuf_bytes(L, T, single);
+  const size_t base = kHdrBytes + hbuf_bytes(L, T, single);
+  return T >= DUCKMOE_MX_MIN_T ? mx_layout(L, T, single, base).end : base;
 }
 
 // rows per down block: more rows share each h' load, fewer keep registers in check
@@ -934,6 +1391,42 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
   }
 }
 
+template <typename K>
+hipError_t persistent_grid(K kern, int threads, int waves_per_cu, int cap, int &grid) {
+  int per_cu = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
+  if (err != hipSuccess) return err;
+  const int cus = device_cus();
+  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  per_cu = std::max(1, std::min(per_cu, waves_per_cu / (threads / 64)));
+  grid = std::max(1, std::min(cus * per_cu, cap));
+  return hipSuccess;
+}
+
+hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_ROW_TILES;
+  hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
+  const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
+  int grid = 0;
+  hipError_t err = persistent_grid(k_gate_up_mx<WA, RT>, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+                                   max_slots * ((a.I + 16 * RT - 1) / (16 * RT)), grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((k_gate_up_mx<WA, RT>), dim3(grid), dim3(WA * 64), 0, st, a, m);
+  hipLaunchKernelGGL(k_mx_hprep, dim3(max_slots * a.T), dim3(256), 0, st, a, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_ROW_TILES;
+  int grid = 0;
+  hipError_t err = persistent_grid(k_down_mx<WA, RT>, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+                                   (a.H + 16 * RT - 1) / (16 * RT) * kMxGroups, grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((k_down_mx<WA, RT>), dim3(grid), dim3(WA * 64), 0, st, a, m);
+  hipLaunchKernelGGL(k_mx_reduce, dim3((a.T * a.H + 255) / 256), dim3(256), 0, st, a, m);
+  return hipGetLastError();
+}
+
 enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
 
 // Shared argument checks and dispatch of the layer entry points.
@@ -975,6 +1468,23 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   a.in_rms = in_rms;
   a.in_eps = in_eps;
 
+  if (use_mx(T, n_shards)) {
+    const MxLayout l = mx_layout(L, T, single, kHdrBytes + hbuf_bytes(L, T, single));
+    uint8_t *b = reinterpret_cast<uint8_t *>(ws);
+    MxArgs m;
+    m.xh = reinterpret_cast<_Float16 *>(b + l.xh);
+    m.xl = reinterpret_cast<_Float16 *>(b + l.xl);
+    m.xinv = reinterpret_cast<float *>(b + l.xinv);
+    m.hh = reinterpret_cast<_Float16 *>(b + l.hh);
+    m.hl = reinterpret_cast<_Float16 *>(b + l.hl);
+    m.hinv = reinterpret_cast<float *>(b + l.hinv);
+    m.part = reinterpret_cast<float *>(b + l.part);
+    m.Hp = l.Hp;
+    m.Ip = l.Ip;
+    if ((stages & kGateUp) && launch_mx_gate_up(a, m, stream) != hipSuccess) return DUCKMOE_EHIP;
+    if ((stages & kDown) && launch_mx_down(a, m, stream) != hipSuccess) return DUCKMOE_EHIP;
+    return DUCKMOE_OK;
+  }
   if (stages & kGateUp) {
     if (launch_gate_up(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   }

@@ -141,6 +141,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Full 64-lane maximum of non-negative values, returned in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_src<0xB1>(v));
+  v = fmaxf(v, dpp_src<0x4E>(v));
+  v = fmaxf(v, dpp_src<0x141>(v));
+  v = fmaxf(v, dpp_src<0x140>(v));
+  v = fmaxf(v, dpp_src<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_src<0x143, 0xC>(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Full 64-lane sum, returned in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum<64>(v);
