@@ -218,8 +218,10 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // gives the same bits as normalizing before it.
 __device__ __forceinline__ float rms_wave_part(const float *row, int H) {
   float ss = 0.0f;
-  if (threadIdx.x < 256)
+  if (threadIdx.x < 256) {
+#pragma unroll 8
     for (int i = threadIdx.x; i < H; i += 256) ss = __builtin_fmaf(row[i], row[i], ss);
+  }
   return wave_sum(ss);
 }
 
@@ -682,9 +684,13 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 // Lane layout (checked on gfx950): A[i][k] is in lane i + 16 * (k / 8), element
 // k % 8; B[k][j] in lane j + 16 * (k / 8), element k % 8; the accumulator
 // element D[i][j] in lane j + 16 * (i / 4), element i % 4.  The k index only has
-// to agree between A and B, so lane group g = lane / 16 takes 32 consecutive
-// columns c .. c + 31 of its row (two 16-byte body loads and 4 sign bytes), and
-// step s of a 128-column unit consumes columns c + 8s .. c + 8s + 7.
+// to agree between A and B.  Weights are loaded so that 4 consecutive lanes
+// read 64 contiguous bytes of one row (lane 4i + q: row i, columns
+// 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15 of the 128-column unit), which
+// the memory pipeline merges; ds_bpermute then moves lane 4i + g's words to
+// lane i + 16g, the MFMA's place for row i and lane group g.  So lane group g
+// holds columns 16g .. 16g + 15 (steps 0, 1) and 64 + 16g .. 64 + 16g + 15
+// (steps 2, 3), and the B loads follow the same columns.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f4v_t __attribute__((ext_vector_type(4)));
 
@@ -692,10 +698,13 @@ constexpr int kMxUnit = 128;   // columns per unit: 4 lane groups x 32
 constexpr int kMxGroups = 8;   // slot groups of the down pass (partials per row)
 constexpr float kLoScale = 2048.0f;
 
+// The hi/lo parts are stored as [column / 8][token][8]: the 8 columns a lane
+// takes for one MFMA step are 16 contiguous bytes, and the lanes of one lane
+// group (consecutive tokens) read consecutive 16-byte pieces.
 struct MxArgs {
-  _Float16 *xh, *xl;  // [T][Hp] scaled activations, hi and lo parts (zero padded)
+  _Float16 *xh, *xl;  // [Hp/8][T][8] scaled activations, hi and lo (zero padded)
   float *xinv;        // [T] 2^-k of each token's scale
-  _Float16 *hh, *hl;  // [slots][T][Ip] scaled h'
+  _Float16 *hh, *hl;  // [slots][Ip/8][T][8] scaled h'
   float *hinv;        // [slots][T]
   float *part;        // [kMxGroups][T][H] down partials
   int Hp, Ip;         // H, I rounded up to whole units
@@ -714,22 +723,37 @@ __device__ __forceinline__ void mx_split(float v, _Float16 &hi, _Float16 &lo) {
   lo = (_Float16)((v - (float)hi) * kLoScale);
 }
 
-// Split one row of n floats (optionally divided by r first) into scaled hi/lo
-// parts of width np (zeros past n); returns 2^-k.  One workgroup of 256 threads.
+// Split one token's row of n floats (optionally divided by r first) into scaled
+// hi/lo parts of width np (zeros past n), stored as [np/8][T][8] at token t;
+// returns 2^-k.  One workgroup of 256 threads.
 __device__ float mx_prep_row(const float *src, int n, int np, float r, _Float16 *hi,
-                             _Float16 *lo, float *red) {
+                             _Float16 *lo, int T, int t, float *red) {
+  // n and np are multiples of 4 (of 16 and 128): float4 loads, 4 per trip
+  const float4 *s4 = reinterpret_cast<const float4 *>(src);
+  const int n4 = n / 4, np4 = np / 4;
   float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(src[i] / r));
+#pragma unroll 4
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = s4[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x / r), fabsf(v.y / r)), fmaxf(fabsf(v.z / r), fabsf(v.w / r))));
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   const int k = mx_scale_exp(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
   const float sc = ldexpf(1.0f, k);
-  for (int i = threadIdx.x; i < np; i += 256) {
-    _Float16 h = (_Float16)0.0f, l = (_Float16)0.0f;
-    if (i < n) mx_split((src[i] / r) * sc, h, l);
-    hi[i] = h;
-    lo[i] = l;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < np4; i += 256) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) v = s4[i];
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    _Float16 h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx_split((e[q] / r) * sc, h[q], l[q]);
+    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+    const size_t o = ((size_t)(i >> 1) * T + t) * 8 + 4 * (i & 1);  // columns 4i .. 4i + 3
+    *reinterpret_cast<h4_t *>(hi + o) = h4_t{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<h4_t *>(lo + o) = h4_t{l[0], l[1], l[2], l[3]};
   }
   return ldexpf(1.0f, -k);
 }
@@ -748,8 +772,7 @@ __global__ __launch_bounds__(256) void k_mx_xprep(const LayerArgs a, const MxArg
     __syncthreads();
     r = rms_divisor(part, a.H, a.in_eps);
   }
-  const float inv = mx_prep_row(row, a.H, m.Hp, r, m.xh + (size_t)t * m.Hp,
-                                m.xl + (size_t)t * m.Hp, red);
+  const float inv = mx_prep_row(row, a.H, m.Hp, r, m.xh, m.xl, a.T, t, red);
   if (threadIdx.x == 0) m.xinv[t] = inv;
 }
 
@@ -761,41 +784,66 @@ __global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArg
   const int slot = blockIdx.x / a.T, t = blockIdx.x - slot * a.T;
   if (slot >= __builtin_amdgcn_readfirstlane(plan[0])) return;
   const size_t rowi = (size_t)slot * a.T + t;
-  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hh + rowi * m.Ip,
-                                m.hl + rowi * m.Ip, red);
+  const size_t blk = (size_t)slot * a.T * m.Ip;  // the slot's [Ip/8][T][8] block
+  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hh + blk, m.hl + blk,
+                                a.T, t, red);
   if (threadIdx.x == 0) m.hinv[rowi] = inv;
 }
 
 struct MxTile {     // one unit of one 16-row block for one lane
-  uint4 b0, b1;     // 32 body bytes: columns c .. c + 31
+  uint4 b0, b1;     // 2 x 16 body bytes (see the layout note)
   uint32_t s0, s1;  // their sign bits (16 + 16)
 };
 
+// Load lane 4i + q's share: row `row` (= the tile's row i), columns
+// c0 + 16q .. and c0 + 64 + 16q .. (16 each).
 __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
                                           __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
-                                          uint32_t c, bool rv) {
-  const bool v0 = rv && c < K, v1 = rv && c + 16 < K;
+                                          uint32_t c0, bool rv) {
+  const uint32_t c = c0 + 16 * (threadIdx.x & 3);
+  const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
   w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
-  w.b1 = buf_load16(rb, v1 ? row * K + c + 16 : kOutOfRange);
+  w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
   w.s0 = buf_load2(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
-  w.s1 = buf_load2(rs, v1 ? row * (K / 8) + c / 8 + 2 : kOutOfRange);
+  w.s1 = buf_load2(rs, v1 ? row * (K / 8) + c / 8 + 8 : kOutOfRange);
+}
+
+// Move lane 4i + g's tile words to lane i + 16g.
+__device__ __forceinline__ MxTile mx_to_mfma(const MxTile &w) {
+  const int l = threadIdx.x & 63;
+  const int src = 4 * ((4 * (l & 15) + (l >> 4)) & 63);  // byte address of lane 4(l % 16) + l / 16
+  auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
+  MxTile o;
+  o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
+  o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
+  const uint32_t sg = mv(w.s0 | (w.s1 << 16));
+  o.s0 = sg & 0xFFFFu;
+  o.s1 = sg >> 16;
+  return o;
 }
 
 struct MxAct {      // the lane's 32 activations of one unit, hi and lo
   uint4 h[4], l[4];
 };
 
+// B for lane (token j, group g): columns c0 + 16g + 8s (s = 0, 1) and
+// c0 + 64 + 16g + 8(s - 2) (s = 2, 3), from a [cols/8][T][8] block at byte base.
 __device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t rh,
-                                          __amdgpu_buffer_rsrc_t rl, uint32_t off, bool v) {
+                                          __amdgpu_buffer_rsrc_t rl, uint32_t base, uint32_t c0,
+                                          int T, bool v) {
+  const int j = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    b.h[s] = buf_load16(rh, v ? off + 16 * s : kOutOfRange);
-    b.l[s] = buf_load16(rl, v ? off + 16 * s : kOutOfRange);
+    const uint32_t kb = (c0 + 16 * g) / 8 + (s & 1) + 8 * (s >> 1);
+    const uint32_t o = base + (kb * (uint32_t)T + j) * 16u;
+    b.h[s] = buf_load16(rh, v ? o : kOutOfRange);
+    b.l[s] = buf_load16(rl, v ? o : kOutOfRange);
   }
 }
 
 // acc_hi += A * B_hi, acc_lo += A * B_lo over the unit's 4 steps
-__device__ __forceinline__ void mx_mma(const MxTile &w, const MxAct &b, f4v_t &ah, f4v_t &al) {
+__device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &ah, f4v_t &al) {
+  const MxTile w = mx_to_mfma(wl);
   h2_t d[16];
   fp9_decode16(w.b0, w.s0, d);
   fp9_decode16(w.b1, w.s1, d + 8);
@@ -820,21 +868,6 @@ struct MxItem {
   int u;  // unit index, -1 for the empty item
 };
 
-__device__ __forceinline__ MxItem mx_first(int wave, int nu) {
-  return MxItem{(int)blockIdx.x, wave < nu ? wave : -1};
-}
-
-template <int WA>
-__device__ __forceinline__ MxItem mx_next(MxItem it, int wave, int nu) {
-  if (it.u >= 0 && it.u + WA < nu) return MxItem{it.task, it.u + WA};
-  return MxItem{it.task + (int)gridDim.x, wave < nu ? wave : -1};
-}
-
-template <int WA>
-__device__ __forceinline__ bool mx_last(MxItem it, int nu) {
-  return it.u < 0 || it.u + WA >= nu;
-}
-
 // Gate/up: a workgroup of WA waves takes whole tasks (slot, block of 16 * RT
 // rows) and splits the task's units (128 columns of H) over its waves; the
 // waves' partial accumulators meet in LDS, wave 0 sums them in a fixed order and
@@ -857,6 +890,12 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   const WavePlan plan = wave_plan(a, pin);
   if (blockIdx.x == 0 && wave == 0) plan_store(plan, a);
   const int ntask = plan.n_slots * NB;
+  // tasks blockIdx.x, blockIdx.x + gridDim.x, ...
+  auto first = [&]() { return MxItem{(int)blockIdx.x, wave < nu ? wave : -1}; };
+  auto next = [&](MxItem it) {
+    if (it.u >= 0 && it.u + WA < nu) return MxItem{it.task, it.u + WA};
+    return MxItem{it.task + (int)gridDim.x, wave < nu ? wave : -1};
+  };
   const int j = lane & 15, g = lane >> 4;
   const uint32_t mat = (uint32_t)I * (uint32_t)H;
   const __amdgpu_buffer_rsrc_t rxh = make_rsrc(m.xh, (uint32_t)(T * m.Hp) * 2u);
@@ -869,14 +908,14 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
     const int e = plan_expert(plan, slot);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
-    const uint32_t c = (uint32_t)(it.u * kMxUnit + 32 * g);
+    const uint32_t c0 = (uint32_t)(it.u * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int row = r0 + 16 * t + j;
-      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c, row < I);
-      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c, row < I);
+      const int row = r0 + 16 * t + (lane >> 2);
+      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c0, row < I);
+      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, row < I);
     }
-    mx_load_b(bf.b, rxh, rxl, ((uint32_t)j * m.Hp + c) * 2u, jv);
+    mx_load_b(bf.b, rxh, rxl, 0u, c0, T, jv);
   };
 
   f4v_t acc[RT][4];
@@ -897,7 +936,7 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
         mx_mma(bf.u[t], bf.b, acc[t][2], acc[t][3]);
       }
     }
-    if (!mx_last<WA>(it, nu)) return;
+    if (it.u >= 0 && it.u + WA < nu) return;
     // close the task: partials to LDS, wave 0 reduces and writes h'
 #pragma unroll
     for (int t = 0; t < RT; ++t)
@@ -939,14 +978,14 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   };
 
   GuMxBuf<WA, RT> b0, b1;
-  MxItem i0 = mx_first(wave, nu), i1;
+  MxItem i0 = first(), i1;
   if (i0.task < ntask) issue(b0, i0);
   while (i0.task < ntask) {
-    i1 = mx_next<WA>(i0, wave, nu);
+    i1 = next(i0);
     if (i1.task < ntask) issue(b1, i1);
     consume(b0, i0);
     if (i1.task >= ntask) break;
-    i0 = mx_next<WA>(i1, wave, nu);
+    i0 = next(i1);
     if (i0.task < ntask) issue(b0, i0);
     consume(b1, i1);
   }
@@ -1006,13 +1045,13 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
     const int e = __builtin_amdgcn_readfirstlane(plan[1 + slot]);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
-    const uint32_t c = (uint32_t)(v * kMxUnit + 32 * g);
+    const uint32_t c0 = (uint32_t)(v * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int row = blk * 16 * RT + 16 * t + j;
-      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c, row < H);
+      const int row = blk * 16 * RT + 16 * t + (lane >> 2);
+      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c0, row < H);
     }
-    mx_load_b(bf.b, rhh, rhl, ((uint32_t)(slot * T + j) * m.Ip + c) * 2u, jv);
+    mx_load_b(bf.b, rhh, rhl, (uint32_t)(slot * T * m.Ip) * 2u, c0, T, jv);
     bf.hs = jv ? m.hinv[slot * T + j] : 0.0f;
   };
 
