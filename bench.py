@@ -269,6 +269,52 @@ def time_pair(torch, dm, layer, steps, warmup, draws):
     return res
 
 
+def time_expert_and_partials(torch, dm, layer, steps, warmup):
+    """One expert at bsz 1 (49.5 MB) and the bsz-2 layer in 32-shard partial mode."""
+    from bit_moe_expert_fp9_amd import synth
+    stream = torch.cuda.current_stream()
+    res = {}
+    x1 = torch.from_numpy(synth.activations(SEED, 2, 0, 0, 1, H)).cuda()
+    out1 = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws1 = layer.workspace(1)
+    e = 17
+    for _ in range(warmup):
+        dm.expert_ffn(layer, e, x1, out=out1, ws=ws1, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(steps):  # a different expert each call, so HBM is read
+        dm.expert_ffn(layer, k % E, x1, out=out1, ws=ws1, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    eb = layer.expert_bytes()
+    res["one_expert_bsz1"] = {"us": us, "hbm_gbps": eb / (us * 1e-6) / 1e9, "bytes": eb}
+    n = steps + warmup
+    X = torch.from_numpy(np.stack([synth.activations(SEED, WORKLOAD, 0, 60_000 + s, 2, H)
+                                   for s in range(n)])).cuda()
+    r = [synth.routing(SEED, WORKLOAD, 0, 60_000 + s, 2, E, K) for s in range(n)]
+    IDS = torch.from_numpy(np.stack([p for p, _ in r])).cuda()
+    W = torch.from_numpy(np.stack([q for _, q in r])).cuda()
+    by = float(np.mean([(len(np.unique(p)) + 1) * eb for p, _ in r[warmup:]]))
+    outp = torch.empty((32, 2, H), dtype=torch.float32, device="cuda")
+    wsp = layer.workspace(2, 32)
+    for s in range(warmup):
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=outp, n_shards=32, ws=wsp, stream=stream)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(steps):
+        s = warmup + k
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=outp, n_shards=32, ws=wsp, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    res["pair_32_partials_bsz2"] = {"us": us, "tokens_per_s": 2 / (us * 1e-6),
+                                    "hbm_gbps": by / (us * 1e-6) / 1e9}
+    log("expert / partials:", json.dumps(res))
+    return res
+
+
 DENSE_I, DENSE_WORKLOAD = 18432, 6
 
 
@@ -433,6 +479,7 @@ def main():
 
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
     pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
+    extra = time_expert_and_partials(torch, dm, layer, min(args.steps, 300), 20)
 
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
     ceil = read_ceiling(torch, dm, [int(r1["bytes_step"]), int(st1["gate_up_bytes"])])
@@ -470,6 +517,7 @@ def main():
             "layer_frac_of_read_ceiling": gbps / lay_gbps,
             "dense_mlp": dense,
             "pair_two_tokens": pair,
+            "expert_and_partials": extra,
             "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {

@@ -405,3 +405,16 @@ def test_read_probe_runs(torch_dev):
         dm.read_probe(buf, nb, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
+
+
+def test_shard_partials_at_larger_batch(torch_dev, small_layers):
+    """Shard partials at T = 4 (the vector kernels; the matrix-core path has no
+    partial mode): each shard and their sum against the oracle."""
+    torch = torch_dev
+    lay, ox = small_layers[103]
+    say("shard partials at T = 4")
+    x, ids, w, got = run_layer_case(torch, lay, ox, 103, 77, 4, n_shards=8)
+    ref = oracle.moe_partials(ox, x, ids, w, lay.n_routed, 8)
+    for r in range(8):
+        check_close(got[r], ref[r], "T=4 shard %d/8" % r)
+    check_close(got.sum(axis=0), oracle.moe_layer(ox, x, ids, w, lay.n_routed), "T=4 sum of partials")
