@@ -27,6 +27,8 @@ Sources, cited by page title and section:
 * chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2 "两条路线的判断"
   (route one: bsz=2, top_k=8 routed experts per token, near-disjoint sets);
   section 9.5 (the GPU stage normalises between layers: the stack glue).
+* memoir page, section "限制条件" (the fp9 prefill kernel is the open item;
+  contexts up to 2048 tokens): the per-expert token lists of ``prefill_plan``.
 * ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
   "形态一：Mac-to-Mac 张量并行（RDMA）" (TP partial sums are f32).
 
@@ -59,5 +61,6 @@ from .moe import (  # noqa: F401
     moe_slot_weights,
     moe_layer,
     moe_partials,
+    prefill_plan,
     rms_normalize,
 )

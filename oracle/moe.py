@@ -189,3 +189,61 @@ def rms_normalize(v, eps=0.0):
     """
     V = np.atleast_2d(np.asarray(v, dtype=np.float64))
     return V / np.sqrt(np.mean(V * V, axis=1, keepdims=True) + float(eps))
+
+
+def prefill_plan(ids, w, n_routed):
+    """Per-expert token lists of a prefill batch (the grouping of a grouped GEMM).
+
+    The pages leave the larger-T expert path open (memoir page, section
+    "限制条件": the fp9 prefill kernel is far from the machine's peak, and
+    contexts were tested up to 2048 tokens); the lists are the plain grouping
+    of the batch's (token, expert) pairs by expert.  Reading taken:
+
+    * list positions p = 0 .. n_routed: p = 0 is the shared expert (index
+      n_routed), p >= 1 is routed expert p - 1;
+    * list p holds, in ascending token order, every token that uses its expert:
+      all tokens for the shared expert, tokens with at least one ids[t, i] == e
+      for a routed one; each token at most once per list;
+    * the entry's weight is 1 for the shared expert, else the sum of w[t, i]
+      over the positions i where the token lists e (summed in list order);
+    * entries are numbered list by list: offsets[p] is the first entry of list
+      p, offsets[n_routed + 1] the total;
+    * tok_entry[t, 0] is token t's shared entry; tok_entry[t, 1 + i] is the
+      entry of (ids[t, i], t) when i is the first position of that id in the
+      token's list, and -1 for a repeat.
+
+    Returns (offsets [n_routed + 2], tokens [A], weights [A] float64,
+    tok_entry [T, top_k + 1]).  Out-of-range ids are rejected.
+    """
+    ids = np.atleast_2d(np.asarray(ids, dtype=np.int64))
+    w = np.atleast_2d(np.asarray(w, dtype=np.float64))
+    if ids.shape != w.shape:
+        raise ValueError("ids and w disagree")
+    if np.any((ids < 0) | (ids >= n_routed)):
+        raise ValueError("routed expert id out of range")
+    T, K = ids.shape
+    lists = [[(t, 1.0) for t in range(T)]]
+    for e in range(n_routed):
+        lst = []
+        for t in range(T):
+            hit = [i for i in range(K) if ids[t, i] == e]
+            if hit:
+                s = 0.0
+                for i in hit:
+                    s += w[t, i]
+                lst.append((t, s))
+        lists.append(lst)
+    offsets = np.zeros(n_routed + 2, dtype=np.int64)
+    for p, lst in enumerate(lists):
+        offsets[p + 1] = offsets[p] + len(lst)
+    tokens = np.array([t for lst in lists for t, _ in lst], dtype=np.int64)
+    weights = np.array([s for lst in lists for _, s in lst], dtype=np.float64)
+    tok_entry = np.full((T, K + 1), -1, dtype=np.int64)
+    for p, lst in enumerate(lists):
+        for r, (t, _) in enumerate(lst):
+            if p == 0:
+                tok_entry[t, 0] = offsets[0] + r
+            else:
+                first = min(i for i in range(K) if ids[t, i] == p - 1)
+                tok_entry[t, 1 + first] = offsets[p] + r
+    return offsets, tokens, weights, tok_entry
