@@ -66,6 +66,10 @@ def parse():
     p.add_argument("--stack-steps", type=int, default=100)
     p.add_argument("--dense", type=int, default=1,
                    help="also time the dense fp9 MLP 7168/18432 at bsz 1 and 2 (0 to skip)")
+    p.add_argument("--prefill", type=str, default="2048",
+                   help="comma-separated token counts for the prefill path on the same layer "
+                        "('' to skip); results go under config.prefill")
+    p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="first run 3 plain device copies of this many MiB (a known-size "
                         "reference for HBM byte counters under rocprofv3 --pmc)")
@@ -315,6 +319,48 @@ def time_expert_and_partials(torch, dm, layer, steps, warmup):
     return res
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def time_prefill(torch, dm, layer, T, steps, warmup, draws=4):
+    """The prefill path (token lists + grouped GEMMs) on T tokens of the same
+    layer: a few seeded draws, cycled, with HIP events around the call."""
+    from bit_moe_expert_fp9_amd import synth
+    stream = torch.cuda.current_stream()
+    xs, ids, ws_, uniq = [], [], [], []
+    for d in range(draws):
+        xs.append(torch.from_numpy(synth.activations(SEED, 7, 0, d, T, H)).cuda())
+        i, w = synth.routing(SEED, 7, 0, d, T, E, K)
+        ids.append(torch.from_numpy(i).cuda())
+        ws_.append(torch.from_numpy(w).cuda())
+        uniq.append(len(np.unique(i)))
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = layer.prefill_workspace(T)
+    for s in range(warmup):
+        dm.moe_prefill(layer, xs[s % draws], ids[s % draws], ws_[s % draws], out=out, ws=ws,
+                       stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for k in range(steps):
+        d = k % draws
+        dm.moe_prefill(layer, xs[d], ids[d], ws_[d], out=out, ws=ws, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    eb = layer.expert_bytes()
+    wbytes = float(np.mean([(u + 1) * eb for u in uniq]))
+    flops = 2.0 * 3 * H * I * T * (K + 1)     # every (token, expert) pair: gate, up, down
+    res = {"T": T, "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+           "weight_bytes": wbytes, "weight_gbps": wbytes / (ms * 1e-3) / 1e9,
+           "weight_hbm_frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "useful_tflops": flops / (ms * 1e-3) / 1e12,
+           "useful_mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+           "mean_experts": float(np.mean(uniq)) + 1}
+    log("prefill T=%d:" % T, json.dumps(res))
+    return res
+
+
 DENSE_I, DENSE_WORKLOAD = 18432, 6
 
 
@@ -480,6 +526,9 @@ def main():
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
     pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
     extra = time_expert_and_partials(torch, dm, layer, min(args.steps, 300), 20)
+    prefill = {}
+    for tok in [int(v) for v in args.prefill.split(",") if v.strip()]:
+        prefill[str(tok)] = time_prefill(torch, dm, layer, tok, args.prefill_steps, 3)
 
     gbps = r1["bytes_step"] / (r1["ms_per_step"] * 1e-3) / 1e9
     ceil = read_ceiling(torch, dm, [int(r1["bytes_step"]), int(st1["gate_up_bytes"])])
@@ -518,6 +567,7 @@ def main():
             "dense_mlp": dense,
             "pair_two_tokens": pair,
             "expert_and_partials": extra,
+            "prefill": prefill or None,
             "k_down_gbps": st1["down_gbps"],
         },
         "roofline": {

@@ -23,7 +23,9 @@ from .duckmoe import (  # noqa: F401
     moe_gate_up,
     moe_layer,
     moe_plan,
+    moe_prefill,
     moe_stack,
+    prefill_plan,
     quantize_fp9,
     quantize_fp9_device,
     read_probe,

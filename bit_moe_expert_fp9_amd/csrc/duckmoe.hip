@@ -41,6 +41,8 @@
 
 #include "../../include/duckmoe.h"
 #include "fp9_device.h"
+#include "host_util.h"
+#include "mfma_device.h"
 
 namespace duckmoe {
 namespace {
@@ -208,8 +210,6 @@ __device__ __forceinline__ void plan_store(const WavePlan &p, const LayerArgs &a
   }
   if (lane < p.n_slots - 1) dst[2 + lane] = p.expert;
 }
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // The RMS glue's sum of squares of one row in a fixed order: thread j < 256
 // adds x[j], x[j + 256], ... with fused multiply-adds; each of the 4 waves sums
@@ -691,10 +691,6 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 // lane i + 16g, the MFMA's place for row i and lane group g.  So lane group g
 // holds columns 16g .. 16g + 15 (steps 0, 1) and 64 + 16g .. 64 + 16g + 15
 // (steps 2, 3), and the B loads follow the same columns.
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float f4v_t __attribute__((ext_vector_type(4)));
-
-constexpr int kMxUnit = 128;   // columns per unit: 4 lane groups x 32
 constexpr int kMxGroups = 8;   // slot groups of the down pass (partials per row)
 constexpr float kLoScale = 2048.0f;
 
@@ -709,14 +705,6 @@ struct MxArgs {
   float *part;        // [kMxGroups][T][H] down partials
   int Hp, Ip;         // H, I rounded up to whole units
 };
-
-// power-of-two scale 2^k with max * 2^k in [2^13, 2^14) (k clamped to +-126)
-__device__ __forceinline__ int mx_scale_exp(float m) {
-  if (!(m > 0.0f)) return 0;
-  int e;
-  frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
-  return max(-126, min(126, 14 - e));
-}
 
 __device__ __forceinline__ void mx_split(float v, _Float16 &hi, _Float16 &lo) {
   hi = (_Float16)v;
@@ -788,38 +776,6 @@ __global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArg
   const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hh + blk, m.hl + blk,
                                 a.T, t, red);
   if (threadIdx.x == 0) m.hinv[rowi] = inv;
-}
-
-struct MxTile {     // one unit of one 16-row block for one lane
-  uint4 b0, b1;     // 2 x 16 body bytes (see the layout note)
-  uint32_t s0, s1;  // their sign bits (16 + 16)
-};
-
-// Load lane 4i + q's share: row `row` (= the tile's row i), columns
-// c0 + 16q .. and c0 + 64 + 16q .. (16 each).
-__device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
-                                          __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
-                                          uint32_t c0, bool rv) {
-  const uint32_t c = c0 + 16 * (threadIdx.x & 3);
-  const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
-  w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
-  w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
-  w.s0 = buf_load2(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
-  w.s1 = buf_load2(rs, v1 ? row * (K / 8) + c / 8 + 8 : kOutOfRange);
-}
-
-// Move lane 4i + g's tile words to lane i + 16g.
-__device__ __forceinline__ MxTile mx_to_mfma(const MxTile &w) {
-  const int l = threadIdx.x & 63;
-  const int src = 4 * ((4 * (l & 15) + (l >> 4)) & 63);  // byte address of lane 4(l % 16) + l / 16
-  auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
-  MxTile o;
-  o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
-  o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
-  const uint32_t sg = mv(w.s0 | (w.s1 << 16));
-  o.s0 = sg & 0xFFFFu;
-  o.s1 = sg >> 16;
-  return o;
 }
 
 struct MxAct {      // the lane's 32 activations of one unit, hi and lo
@@ -1227,7 +1183,6 @@ __global__ __launch_bounds__(512) void k_read_probe(const uint4 *__restrict__ p,
 }
 
 // ------------------------------------------------------------ host side ----
-bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
 constexpr size_t kGuXLds = 131072;  // LDS bytes for the activations of one gate/up pass
 
@@ -1348,23 +1303,6 @@ constexpr int down_rows() {
   return T == 1 ? DUCKMOE_DN_ROWS : (T == 2 ? 2 * DUCKMOE_DN_ROWS : (T <= 4 ? DUCKMOE_DN_ROWS : 2));
 }
 
-// Compute units of the current device, cached per device id.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return -1;
-  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
 template <int TG>
 hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
   constexpr int P = DUCKMOE_GU_PAIRS, WA = DUCKMOE_GU_WAVES;
@@ -1428,18 +1366,6 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
     case 7: return launch_down_t<7>(a, st);
     default: return launch_down_t<8>(a, st);
   }
-}
-
-template <typename K>
-hipError_t persistent_grid(K kern, int threads, int waves_per_cu, int cap, int &grid) {
-  int per_cu = 0;
-  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
-  if (err != hipSuccess) return err;
-  const int cus = device_cus();
-  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
-  per_cu = std::max(1, std::min(per_cu, waves_per_cu / (threads / 64)));
-  grid = std::max(1, std::min(cus * per_cu, cap));
-  return hipSuccess;
 }
 
 hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {

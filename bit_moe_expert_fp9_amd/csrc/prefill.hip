@@ -1,0 +1,776 @@
+// prefill.hip - the larger-T (prefill) routed layer: per-expert token lists and
+// a grouped GEMM on the matrix cores.
+//
+// What is computed is the routed layer of duckmoe.hip, for many tokens at once:
+// out_t = shared(x_t) + sum_i w_ti expert_{ids_ti}(x_t) with the SwiGLU experts
+// in fp9 (duck-llm memoir page "一鸭三吃：我把评测鸭变成了满血 DeepSeek-V3.2 推理
+// 系统", fp9 section "在只有 AVX2 的 N100 上，我先做出了单核 MLP fp9"; chapter
+// page "第 9 章 MTP1 dual-lane overlap", section 9.2 "两条路线的判断" for top-8
+// routing plus the shared expert).  The pages name the fp9 prefill kernel as
+// the part still far from peak (memoir page, section "限制条件", which also
+// tests contexts up to 2048 tokens); this file is that path on gfx950.
+//
+// Decode streams every selected expert once per step; at prefill sizes an
+// expert serves many tokens, so its weights should be read once for all of
+// them.  The tokens are grouped by expert:
+//   k_pf_count / k_pf_scan / k_pf_fill: list p = 0 is the shared expert (every
+//     token, weight 1), list p >= 1 routed expert p - 1 with the tokens that
+//     name it in ascending order (a repeated id adds its weights; an id out of
+//     range is skipped; both are flagged in the status word).  Entries are
+//     numbered list by list; tok_entry[t] names token t's entries (shared
+//     first, then by id position, -1 for a repeat or a bad id).  Lists are cut
+//     into tiles of 64 entries.  Only per-list scans, a block scan and a
+//     ballot: no atomics, the same lists every call.
+//   k_pf_xprep: x rows -> fp16 hi/lo pairs (below).
+//   k_pf_gate_up: a workgroup of 8 waves takes tasks (tile, block of 256
+//     intermediate rows): each wave owns 32 gate rows and the matching 32 up
+//     rows, the tile's activations of each 128-column unit are staged once in
+//     LDS for all 8 waves, and the epilogue writes h' = w * silu(gate) * up as
+//     scaled fp16 hi/lo pairs per (entry, 128-row unit).
+//   k_pf_down: the same grouped GEMM over (tile, block of 256 output rows) with
+//     the down weights, writing y[entry][H] in f32.
+//   k_pf_combine: out_t = the entries of tok_entry[t] added in slot order.
+// Every output element is a fixed-order sum: bit-identical run to run.
+//
+// Precision.  fp9 -> fp16 is exact (A operand).  An f32 activation v (B) is
+// carried as hi = fp16(v s) and lo = fp16(v s - hi), s a power of two per
+// token row (x) or per (entry, 128-row unit) (h') that puts the row's largest
+// magnitude in [2^13, 2^14): both parts stay finite, v s - hi is exact in f32
+// and lo keeps 11 more bits.  A * hi and A * lo go into the same f32
+// accumulator (fp16 x fp16 products are exact in f32), and the scale is
+// undone in f32.  The error is that of a ~22-bit activation plus f32
+// accumulation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/duckmoe.h"
+#include "fp9_device.h"
+#include "host_util.h"
+#include "mfma_device.h"
+
+namespace duckmoe {
+namespace {
+
+constexpr int kPfTile = 64;                     // entries (tokens) per tile
+constexpr int kPfCols = kPfTile / 16;           // MFMA column tiles per tile
+constexpr int kPfWaves = 8;                     // waves per GEMM workgroup
+constexpr int kPfRT = 2;                        // 16-row tiles per wave and matrix
+constexpr int kPfRows = kPfWaves * kPfRT * 16;  // rows per GEMM task
+constexpr int kPfPitch = 2 * kMxUnit + 16;      // LDS bytes per token row of a unit (padded)
+constexpr int kPfMaxTopK = 32;
+constexpr int kPfMaxRouted = 1024;
+constexpr int kPfMaxTokens = 32768;
+static_assert(kPfRT * 16 * 4 == kMxUnit, "4 waves cover one 128-row unit of h'");
+static_assert(kPfWaves * 64 * 4 == 2 * kPfTile * (2 * kMxUnit) / 16,
+              "one workgroup stages a unit's hi/lo tile as 4 x 16 bytes per thread");
+
+struct PfArgs {
+  int H, I, E, K, T, Hp, Ip, A;  // A = entry capacity, T * (K + 1)
+  const uint8_t *gu_body, *gu_sign, *dn_body, *dn_sign;
+  const float *x;        // [T][H]
+  const int32_t *ids;    // [T][K] (K = 0: no routed ids)
+  const float *w;        // [T][K]
+  float *out;            // [T][H]
+  int32_t *status;       // status word
+  int32_t *n_tiles;      // tile count (null: no tile table)
+  int32_t *off;          // [E + 2] first entry of each list
+  int4 *tiles;           // {list, first entry, entries, 0}
+  int32_t *tok;          // [A] token of each entry
+  float *wt;             // [A] routing weight of each entry
+  int32_t *tok_entry;    // [T][K + 1]
+  _Float16 *xh, *xl;     // [T][Hp] scaled x, hi and lo (zero padded)
+  float *xinv;           // [T] 1 / scale
+  _Float16 *hh, *hl;     // [A][Ip] scaled h'
+  float *hs;             // [A][Ip / 128] 1 / scale per 128-row unit
+  float *y;              // [A][H] down outputs per entry
+};
+
+__device__ __forceinline__ int block_sum256(int v, int *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+// ------------------------------------------------------------------ plan ----
+// One workgroup per list.  List 0 (shared) counts every token and checks every
+// token's ids (status word; -1 in tok_entry for repeats and bad ids); list
+// p >= 1 counts the tokens naming expert p - 1.  Counts go to off[p + 1].
+__global__ __launch_bounds__(256) void k_pf_count(const PfArgs a) {
+  __shared__ int red[4];
+  const int p = blockIdx.x, K = a.K, T = a.T;
+  if (p == 0) {
+    int st = 0;
+    for (int t = threadIdx.x; t < T; t += 256) {
+      const int32_t *row = a.ids + (size_t)t * K;
+      for (int i = 0; i < K; ++i) {
+        const int id = row[i];
+        bool keep = id >= 0 && id < a.E;
+        if (!keep) {
+          st |= DUCKMOE_STATUS_BAD_ID;
+        } else {
+          for (int q = 0; q < i; ++q)
+            if (row[q] == id) {
+              keep = false;
+              st |= DUCKMOE_STATUS_DUP_ID;
+              break;
+            }
+        }
+        if (!keep) a.tok_entry[(size_t)t * (K + 1) + 1 + i] = -1;
+      }
+    }
+    const int bad = block_sum256((st & DUCKMOE_STATUS_BAD_ID) ? 1 : 0, red);
+    const int dup = block_sum256((st & DUCKMOE_STATUS_DUP_ID) ? 1 : 0, red);
+    if (threadIdx.x == 0) {
+      a.status[0] = (bad ? DUCKMOE_STATUS_BAD_ID : 0) | (dup ? DUCKMOE_STATUS_DUP_ID : 0);
+      a.off[1] = T;
+    }
+    return;
+  }
+  const int e = p - 1;
+  int c = 0;
+  for (int t = threadIdx.x; t < T; t += 256) {
+    const int32_t *row = a.ids + (size_t)t * K;
+    bool hit = false;
+    for (int i = 0; i < K; ++i) hit |= row[i] == e;
+    c += hit ? 1 : 0;
+  }
+  c = block_sum256(c, red);
+  if (threadIdx.x == 0) a.off[p + 1] = c;
+}
+
+// One workgroup of 1024: counts -> first entries (exclusive scan over lists),
+// the tile table (lists cut into tiles of kPfTile entries) and its size.
+__global__ __launch_bounds__(1024) void k_pf_scan(const PfArgs a) {
+  __shared__ int cnt[kPfMaxRouted + 1];
+  __shared__ int se[1024], st[1024];
+  const int n = a.E + 1, tid = threadIdx.x;
+  for (int p = tid; p < n; p += 1024) cnt[p] = a.off[p + 1];
+  __syncthreads();
+  const int per = (n + 1023) / 1024, p0 = min(n, tid * per), p1 = min(n, p0 + per);
+  int ce = 0, ct = 0;
+  for (int p = p0; p < p1; ++p) {
+    ce += cnt[p];
+    ct += (cnt[p] + kPfTile - 1) / kPfTile;
+  }
+  se[tid] = ce;
+  st[tid] = ct;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int ve = tid >= d ? se[tid - d] : 0, vt = tid >= d ? st[tid - d] : 0;
+    __syncthreads();
+    se[tid] += ve;
+    st[tid] += vt;
+    __syncthreads();
+  }
+  int eb = se[tid] - ce, tb = st[tid] - ct;
+  for (int p = p0; p < p1; ++p) {
+    a.off[p] = eb;
+    if (a.tiles) {
+      for (int k = 0; k * kPfTile < cnt[p]; ++k)
+        a.tiles[tb + k] = make_int4(p, eb + k * kPfTile, min(kPfTile, cnt[p] - k * kPfTile), 0);
+    }
+    tb += (cnt[p] + kPfTile - 1) / kPfTile;
+    eb += cnt[p];
+  }
+  if (tid == 1023) {
+    a.off[n] = se[1023];
+    if (a.n_tiles) *a.n_tiles = st[1023];
+  }
+}
+
+// One workgroup per list: the list's tokens in ascending order, 256 at a time;
+// a token's rank is the hits before it (ballot within the wave, wave counts
+// across the workgroup).
+__global__ __launch_bounds__(256) void k_pf_fill(const PfArgs a) {
+  __shared__ int wc[4];
+  const int p = blockIdx.x, K = a.K, T = a.T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = a.off[p];
+  if (p == 0) {
+    for (int t = threadIdx.x; t < T; t += 256) {
+      a.tok[base + t] = t;
+      a.wt[base + t] = 1.0f;
+      a.tok_entry[(size_t)t * (K + 1)] = base + t;
+    }
+    return;
+  }
+  const int e = p - 1;
+  int run = 0;
+  for (int t0 = 0; t0 < T; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    bool hit = false;
+    int first = 0;
+    float s = 0.0f;
+    if (t < T) {
+      const int32_t *row = a.ids + (size_t)t * K;
+      const float *wr = a.w + (size_t)t * K;
+      for (int i = 0; i < K; ++i) {
+        if (row[i] == e) {
+          if (!hit) first = i;
+          hit = true;
+          s += wr[i];
+        }
+      }
+    }
+    const uint64_t m = __ballot(hit);
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wc[wave] = __popcll(m);
+    __syncthreads();
+    int before = run;
+    for (int q = 0; q < wave; ++q) before += wc[q];
+    if (hit) {
+      const int ent = base + before + rank;
+      a.tok[ent] = t;
+      a.wt[ent] = s;
+      a.tok_entry[(size_t)t * (K + 1) + 1 + first] = ent;
+    }
+    run += wc[0] + wc[1] + wc[2] + wc[3];
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------- x prep ----
+// One workgroup per token: x row -> scaled hi/lo fp16 rows of width Hp.
+__global__ __launch_bounds__(256) void k_pf_xprep(const PfArgs a) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float4 *s4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H);
+  const int n4 = a.H / 4, np4 = a.Hp / 4;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = s4[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const int k = mx_scale_exp(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  const float sc = ldexpf(1.0f, k);
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  for (int i = threadIdx.x; i < np4; i += 256) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) v = s4[i];
+    const float e[4] = {v.x * sc, v.y * sc, v.z * sc, v.w * sc};
+    h4_t hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hi[q] = (_Float16)e[q];
+      lo[q] = (_Float16)(e[q] - (float)hi[q]);
+    }
+    const size_t o = (size_t)t * a.Hp + 4 * i;
+    *reinterpret_cast<h4_t *>(a.xh + o) = hi;
+    *reinterpret_cast<h4_t *>(a.xl + o) = lo;
+  }
+  if (threadIdx.x == 0) a.xinv[t] = ldexpf(1.0f, -k);
+}
+
+// ------------------------------------------------------- grouped GEMMs ----
+// Workgroups are dispatched to the 8 XCDs round robin; virtual ids that are
+// consecutive within a round stay on one XCD, so the tasks of one tile (which
+// read the same activations) share that XCD's L2.
+__device__ __forceinline__ int pf_vid() {
+  const int G = gridDim.x, b = blockIdx.x;
+  if (G % 8) return b;
+  return (b % 8) * (G / 8) + b / 8;
+}
+
+// B staging: a unit's tile is [2 parts][64 tokens][256 bytes]; thread tid moves
+// the 16-byte pieces (part h, token tid / 16 + 32 q, bytes 16 (tid % 16) ..)
+// for h, q in {0, 1}: global -> registers, then registers -> LDS.
+struct PfStage {
+  uint4 v[2][2];
+};
+
+__device__ __forceinline__ void pf_stage_load(PfStage &s, __amdgpu_buffer_rsrc_t rh,
+                                              __amdgpu_buffer_rsrc_t rl, const uint32_t src[2],
+                                              uint32_t ubytes) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t o = src[q] == kOutOfRange ? kOutOfRange : src[q] + ubytes;
+    s.v[0][q] = buf_load16(rh, o);
+    s.v[1][q] = buf_load16(rl, o);
+  }
+}
+
+__device__ __forceinline__ void pf_stage_store(const PfStage &s, uint8_t *buf) {
+  const int tok = threadIdx.x >> 4, seg = threadIdx.x & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<uint4 *>(buf + h * (kPfTile * kPfPitch) + (tok + 32 * q) * kPfPitch +
+                                 seg * 16) = s.v[h][q];
+}
+
+// MFMA B operand of lane (token j, group g) for column tile ct and step s.
+__device__ __forceinline__ half8_t pf_b(const uint8_t *buf, int part, int ct, int s) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int seg = 2 * g + (s & 1) + 8 * (s >> 1);
+  return *reinterpret_cast<const half8_t *>(buf + part * (kPfTile * kPfPitch) +
+                                            (16 * ct + j) * kPfPitch + seg * 16);
+}
+
+__device__ __forceinline__ half8_t pf_a(const h2_t d[8], int ss) {
+  return __builtin_bit_cast(half8_t, make_uint4(__builtin_bit_cast(uint32_t, d[4 * ss]),
+                                                __builtin_bit_cast(uint32_t, d[4 * ss + 1]),
+                                                __builtin_bit_cast(uint32_t, d[4 * ss + 2]),
+                                                __builtin_bit_cast(uint32_t, d[4 * ss + 3])));
+}
+
+// acc[r][m][ct] += A(r, m) * B(ct) over one 128-column unit.  M matrices of
+// RT row tiles each; wm holds the unit's weight tiles in MFMA order; only the
+// first nct column tiles are live.
+template <int RT, int M>
+__device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t *buf, int nct,
+                                        f4v_t (&acc)[RT][M][kPfCols]) {
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    h2_t d[RT][M][8];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        fp9_decode16(hf ? wm[r][m].b1 : wm[r][m].b0, hf ? wm[r][m].s1 : wm[r][m].s0, d[r][m]);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const int s = 2 * hf + ss;
+#pragma unroll
+      for (int ct = 0; ct < kPfCols; ++ct) {
+        if (ct < nct) {
+          const half8_t bh = pf_b(buf, 0, ct, s), bl = pf_b(buf, 1, ct, s);
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              const half8_t A = pf_a(d[r][m], ss);
+              acc[r][m][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, acc[r][m][ct], 0, 0, 0);
+              acc[r][m][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, acc[r][m][ct], 0, 0, 0);
+            }
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int4 pf_tile(const PfArgs &a, int tile) {
+  const int4 t = a.tiles[tile];
+  return make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
+                   __builtin_amdgcn_readfirstlane(t.z), 0);
+}
+
+// Gate/up: task = (tile, block of kPfRows intermediate rows).
+__global__ __launch_bounds__(kPfWaves * 64) void k_pf_gate_up(const PfArgs a) {
+  constexpr int RT = kPfRT, NT = kPfCols;
+  __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * kPfTile * kPfPitch];
+  __shared__ float red[kPfWaves][kPfTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I;
+  const int NB = (I + kPfRows - 1) / kPfRows;
+  const int ntask = __builtin_amdgcn_readfirstlane(*a.n_tiles) * NB;
+  const int nu = a.Hp / kMxUnit, nv = a.Ip / kMxUnit;
+  const uint32_t mat = (uint32_t)I * (uint32_t)H;
+  const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.xh, (uint32_t)a.T * (uint32_t)a.Hp * 2u);
+  const __amdgpu_buffer_rsrc_t rxl = make_rsrc(a.xl, (uint32_t)a.T * (uint32_t)a.Hp * 2u);
+
+  for (int task = pf_vid(); task < ntask; task += gridDim.x) {
+    const int tile = task / NB, blk = task - tile * NB;
+    const int4 tl = pf_tile(a, tile);
+    const int e0 = tl.y, n = tl.z, nct = (n + 15) / 16;
+    const int ex = tl.x == 0 ? a.E : tl.x - 1;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)ex * 2 * mat, 2 * mat);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.gu_sign + (size_t)ex * 2 * (mat / 8), 2 * (mat / 8));
+    uint32_t src[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tt = (threadIdx.x >> 4) + 32 * q;
+      src[q] = tt < n ? ((uint32_t)a.tok[e0 + tt] * (uint32_t)a.Hp + 8u * (threadIdx.x & 15)) * 2u
+                      : kOutOfRange;
+    }
+    const int r0 = blk * kPfRows + wave * RT * 16;  // the wave's first row
+    auto load_w = [&](MxTile (&t)[RT][2], int u) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = r0 + 16 * r + (lane >> 2);
+        mx_load_w(t[r][0], rb, rs, (uint32_t)row, H, u * kMxUnit, row < I);
+        mx_load_w(t[r][1], rb, rs, (uint32_t)(I + row), H, u * kMxUnit, row < I);
+      }
+    };
+
+    f4v_t acc[RT][2][NT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[r][m][ct] = f4v_t{0, 0, 0, 0};
+
+    PfStage stg;
+    MxTile raw[RT][2];
+    pf_stage_load(stg, rxh, rxl, src, 0);
+    load_w(raw, 0);
+    pf_stage_store(stg, lb[0]);
+    __syncthreads();
+    for (int u = 0; u < nu; ++u) {
+      const bool more = u + 1 < nu;
+      if (more) pf_stage_load(stg, rxh, rxl, src, (uint32_t)(u + 1) * kMxUnit * 2u);
+      MxTile wm[RT][2];
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
+      if (more) load_w(raw, u + 1);
+      pf_unit<RT, 2>(wm, lb[u & 1], nct, acc);
+      if (more) pf_stage_store(stg, lb[(u + 1) & 1]);
+      __syncthreads();
+    }
+
+    // epilogue: h' = w * silu(gate) * up, then per (entry, 128-row unit) scaled
+    // hi/lo rows; the unit is the 4 waves q0 .. q0 + 3
+    float mx[NT];
+    bool tv[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int tt = 16 * ct + j;
+      tv[ct] = tt < n;
+      const float xs = tv[ct] ? a.xinv[a.tok[e0 + tt]] : 0.0f;
+      const float wv = tv[ct] ? a.wt[e0 + tt] : 0.0f;
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gs = acc[r][0][ct][i] * xs, us = acc[r][1][ct][i] * xs;
+          const float hv = (wv == 0.0f) ? 0.0f : wv * (silu(gs) * us);
+          acc[r][0][ct][i] = hv;
+          m = fmaxf(m, fabsf(hv));
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      mx[ct] = m;
+      if (g == 0) red[wave][16 * ct + j] = m;
+    }
+    __syncthreads();
+    const int q0 = wave & ~3;
+    const int unit = (blk * kPfRows) / kMxUnit + (wave >> 2);
+    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int tt = 16 * ct + j;
+      const float M = fmaxf(fmaxf(red[q0][tt], red[q0 + 1][tt]), fmaxf(red[q0 + 2][tt], red[q0 + 3][tt]));
+      const int k = mx_scale_exp(M);
+      const float sc = ldexpf(1.0f, k);
+      if (tv[ct] && unit < nv) {
+        const size_t rowbase = (size_t)(e0 + tt) * a.Ip;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int row = r0 + 16 * r + 4 * g;
+          h4_t hi, lo;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc[r][0][ct][i] * sc;
+            hi[i] = (_Float16)v;
+            lo[i] = (_Float16)(v - (float)hi[i]);
+          }
+          *reinterpret_cast<h4_t *>(a.hh + rowbase + row) = hi;
+          *reinterpret_cast<h4_t *>(a.hl + rowbase + row) = lo;
+        }
+        if (wave == q0 && g == 0) a.hs[(size_t)(e0 + tt) * nv + unit] = ldexpf(1.0f, -k);
+      }
+      (void)mx[ct];
+    }
+    __syncthreads();
+  }
+}
+
+// Down: task = (tile, block of kPfRows output rows); K = the intermediate
+// dimension in 128-wide units, each unit's h' scale applied after its MFMAs.
+__global__ __launch_bounds__(kPfWaves * 64) void k_pf_down(const PfArgs a) {
+  constexpr int RT = kPfRT, NT = kPfCols;
+  __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * kPfTile * kPfPitch];
+  __shared__ float lsc[2][kPfTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I;
+  const int NB = (H + kPfRows - 1) / kPfRows;
+  const int ntask = __builtin_amdgcn_readfirstlane(*a.n_tiles) * NB;
+  const int nv = a.Ip / kMxUnit;
+  const uint32_t mat = (uint32_t)I * (uint32_t)H;
+  const __amdgpu_buffer_rsrc_t rhh = make_rsrc(a.hh, (uint32_t)a.A * (uint32_t)a.Ip * 2u);
+  const __amdgpu_buffer_rsrc_t rhl = make_rsrc(a.hl, (uint32_t)a.A * (uint32_t)a.Ip * 2u);
+
+  for (int task = pf_vid(); task < ntask; task += gridDim.x) {
+    const int tile = task / NB, blk = task - tile * NB;
+    const int4 tl = pf_tile(a, tile);
+    const int e0 = tl.y, n = tl.z, nct = (n + 15) / 16;
+    const int ex = tl.x == 0 ? a.E : tl.x - 1;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)ex * mat, mat);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)ex * (mat / 8), mat / 8);
+    uint32_t src[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tt = (threadIdx.x >> 4) + 32 * q;
+      src[q] = tt < n ? ((uint32_t)(e0 + tt) * (uint32_t)a.Ip + 8u * (threadIdx.x & 15)) * 2u
+                      : kOutOfRange;
+    }
+    const int r0 = blk * kPfRows + wave * RT * 16;
+    auto load_w = [&](MxTile (&t)[RT][1], int u) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = r0 + 16 * r + (lane >> 2);
+        mx_load_w(t[r][0], rb, rs, (uint32_t)row, I, u * kMxUnit, row < H);
+      }
+    };
+    auto load_sc = [&](int u) {
+      const int tt = threadIdx.x;
+      return (tt < n) ? a.hs[(size_t)(e0 + tt) * nv + u] : 0.0f;
+    };
+
+    f4v_t acc[RT][NT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) acc[r][ct] = f4v_t{0, 0, 0, 0};
+
+    PfStage stg;
+    MxTile raw[RT][1];
+    float scv = 0.0f;
+    pf_stage_load(stg, rhh, rhl, src, 0);
+    if (threadIdx.x < kPfTile) scv = load_sc(0);
+    load_w(raw, 0);
+    pf_stage_store(stg, lb[0]);
+    if (threadIdx.x < kPfTile) lsc[0][threadIdx.x] = scv;
+    __syncthreads();
+    for (int u = 0; u < nv; ++u) {
+      const bool more = u + 1 < nv;
+      if (more) {
+        pf_stage_load(stg, rhh, rhl, src, (uint32_t)(u + 1) * kMxUnit * 2u);
+        if (threadIdx.x < kPfTile) scv = load_sc(u + 1);
+      }
+      MxTile wm[RT][1];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) wm[r][0] = mx_to_mfma(raw[r][0]);
+      if (more) load_w(raw, u + 1);
+      f4v_t tmp[RT][1][NT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
+      pf_unit<RT, 1>(wm, lb[u & 1], nct, tmp);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        if (ct < nct) {
+          const float s = lsc[u & 1][16 * ct + j];
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][ct] += tmp[r][0][ct] * s;
+        }
+      }
+      if (more) {
+        pf_stage_store(stg, lb[(u + 1) & 1]);
+        if (threadIdx.x < kPfTile) lsc[(u + 1) & 1][threadIdx.x] = scv;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int tt = 16 * ct + j;
+      if (tt < n) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int row = r0 + 16 * r + 4 * g;
+          if (row < H)
+            *reinterpret_cast<float4 *>(a.y + (size_t)(e0 + tt) * H + row) =
+                make_float4(acc[r][ct][0], acc[r][ct][1], acc[r][ct][2], acc[r][ct][3]);
+        }
+      }
+    }
+  }
+}
+
+// out[t] = y of token t's entries, shared first, then by id position.
+__global__ __launch_bounds__(256) void k_pf_combine(const PfArgs a) {
+  const int H4 = a.H / 4, K1 = a.K + 1;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)a.T * H4) return;
+  const int t = (int)(i / H4), c = (int)(i - (size_t)t * H4);
+  const int32_t *te = a.tok_entry + (size_t)t * K1;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = 0; q < K1; ++q) {
+    const int ent = te[q];
+    if (ent >= 0) {
+      const float4 v = reinterpret_cast<const float4 *>(a.y + (size_t)ent * a.H)[c];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+  }
+  reinterpret_cast<float4 *>(a.out)[i] = s;
+}
+
+// ------------------------------------------------------------ host side ----
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+struct PfLayout {
+  size_t off, tiles, tok, wt, tok_entry, xh, xl, xinv, hh, hl, hs, y, end;
+  int Hp, Ip, A, K, max_tiles;
+};
+
+PfLayout pf_layout(const duckmoe_layer *L, int T, bool routed) {
+  PfLayout l;
+  l.K = routed ? L->top_k : 0;
+  l.Hp = (L->hidden + kMxUnit - 1) / kMxUnit * kMxUnit;
+  l.Ip = (L->inter + kMxUnit - 1) / kMxUnit * kMxUnit;
+  l.A = T * (l.K + 1);
+  l.max_tiles = (l.A + kPfTile - 1) / kPfTile + L->n_routed + 1;
+  size_t o = 256;  // status word, tile count
+  l.off = o;       o = align256(o + (size_t)(L->n_routed + 2) * 4);
+  l.tiles = o;     o = align256(o + (size_t)l.max_tiles * 16);
+  l.tok = o;       o = align256(o + (size_t)l.A * 4);
+  l.wt = o;        o = align256(o + (size_t)l.A * 4);
+  l.tok_entry = o; o = align256(o + (size_t)T * (l.K + 1) * 4);
+  l.xh = o;        o = align256(o + (size_t)T * l.Hp * 2);
+  l.xl = o;        o = align256(o + (size_t)T * l.Hp * 2);
+  l.xinv = o;      o = align256(o + (size_t)T * 4);
+  l.hh = o;        o = align256(o + (size_t)l.A * l.Ip * 2);
+  l.hl = o;        o = align256(o + (size_t)l.A * l.Ip * 2);
+  l.hs = o;        o = align256(o + (size_t)l.A * (l.Ip / kMxUnit) * 4);
+  l.y = o;         o = align256(o + (size_t)l.A * L->hidden * 4);
+  l.end = o;
+  return l;
+}
+
+int pf_check(const duckmoe_layer *L, int T, bool routed) {
+  if (!L || !L->gu_body || !L->gu_sign || !L->dn_body || !L->dn_sign) return DUCKMOE_EINVAL;
+  if (T < 1 || T > kPfMaxTokens) return DUCKMOE_EINVAL;
+  if (L->hidden < 16 || L->hidden % 16 || L->inter < 16 || L->inter % 16 || L->top_k < 1 ||
+      L->n_routed < 0 || L->n_routed > kPfMaxRouted || (routed && L->top_k > kPfMaxTopK))
+    return DUCKMOE_ESHAPE;
+  if (2ll * L->hidden * L->inter > 0x7fffffffll) return DUCKMOE_ESHAPE;
+  const PfLayout l = pf_layout(L, T, routed);
+  // 32-bit buffer offsets: the staged operands stay below 2 GiB
+  if ((int64_t)T * l.Hp * 2 > 0x7fffffffll || (int64_t)l.A * l.Ip * 2 > 0x7fffffffll)
+    return DUCKMOE_ESHAPE;
+  if (!aligned(L->gu_body, 16) || !aligned(L->dn_body, 16) || !aligned(L->gu_sign, 2) ||
+      !aligned(L->dn_sign, 2))
+    return DUCKMOE_EINVAL;
+  return DUCKMOE_OK;
+}
+
+#ifndef DUCKMOE_PF_WAVES_PER_CU
+#define DUCKMOE_PF_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
+#endif
+
+hipError_t launch_plan(const PfArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pf_count, dim3(a.E + 1), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(k_pf_fill, dim3(a.E + 1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace duckmoe
+
+using namespace duckmoe;
+
+extern "C" {
+
+size_t duckmoe_prefill_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t routed) {
+  if (pf_check(L, T, routed != 0)) return 0;
+  return pf_layout(L, T, routed != 0).end;
+}
+
+int duckmoe_moe_prefill(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                        const float *w, int32_t T, float *out, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  const bool routed = ids != nullptr;
+  int rc = pf_check(L, T, routed);
+  if (rc) return rc;
+  if (routed && !w) return DUCKMOE_EINVAL;
+  if (!x || !out || !ws) return DUCKMOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 256)) return DUCKMOE_EINVAL;
+  const PfLayout l = pf_layout(L, T, routed);
+  if (ws_bytes < l.end) return DUCKMOE_EWORKSPACE;
+  uint8_t *b = reinterpret_cast<uint8_t *>(ws);
+  PfArgs a;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.E = L->n_routed;
+  a.K = l.K;
+  a.T = T;
+  a.Hp = l.Hp;
+  a.Ip = l.Ip;
+  a.A = l.A;
+  a.gu_body = L->gu_body;
+  a.gu_sign = L->gu_sign;
+  a.dn_body = L->dn_body;
+  a.dn_sign = L->dn_sign;
+  a.x = x;
+  a.ids = ids;
+  a.w = w;
+  a.out = out;
+  a.status = reinterpret_cast<int32_t *>(b);
+  a.n_tiles = reinterpret_cast<int32_t *>(b) + 1;
+  a.off = reinterpret_cast<int32_t *>(b + l.off);
+  a.tiles = reinterpret_cast<int4 *>(b + l.tiles);
+  a.tok = reinterpret_cast<int32_t *>(b + l.tok);
+  a.wt = reinterpret_cast<float *>(b + l.wt);
+  a.tok_entry = reinterpret_cast<int32_t *>(b + l.tok_entry);
+  a.xh = reinterpret_cast<_Float16 *>(b + l.xh);
+  a.xl = reinterpret_cast<_Float16 *>(b + l.xl);
+  a.xinv = reinterpret_cast<float *>(b + l.xinv);
+  a.hh = reinterpret_cast<_Float16 *>(b + l.hh);
+  a.hl = reinterpret_cast<_Float16 *>(b + l.hl);
+  a.hs = reinterpret_cast<float *>(b + l.hs);
+  a.y = reinterpret_cast<float *>(b + l.y);
+
+  if (launch_plan(a, stream) != hipSuccess) return DUCKMOE_EHIP;
+  hipLaunchKernelGGL(k_pf_xprep, dim3(T), dim3(256), 0, stream, a);
+  const int threads = kPfWaves * 64;
+  int g1 = 0, g2 = 0;
+  const int NBi = (a.I + kPfRows - 1) / kPfRows, NBh = (a.H + kPfRows - 1) / kPfRows;
+  if (persistent_grid(k_pf_gate_up, threads, DUCKMOE_PF_WAVES_PER_CU, l.max_tiles * NBi, g1) !=
+          hipSuccess ||
+      persistent_grid(k_pf_down, threads, DUCKMOE_PF_WAVES_PER_CU, l.max_tiles * NBh, g2) !=
+          hipSuccess)
+    return DUCKMOE_EHIP;
+  hipLaunchKernelGGL(k_pf_gate_up, dim3(g1), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(k_pf_down, dim3(g2), dim3(threads), 0, stream, a);
+  const size_t n4 = (size_t)T * (a.H / 4);
+  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+int duckmoe_prefill_plan(const int32_t *ids, const float *w, int32_t T, int32_t top_k,
+                         int32_t n_routed, int32_t *offsets, int32_t *tokens, float *weights,
+                         int32_t *tok_entry, int32_t *status, hipStream_t stream) {
+  if (T < 1 || T > kPfMaxTokens || top_k < 0 || top_k > kPfMaxTopK || n_routed < 0 ||
+      n_routed > kPfMaxRouted)
+    return DUCKMOE_EINVAL;
+  if ((top_k > 0 && (!ids || !w)) || !offsets || !tokens || !weights || !tok_entry || !status)
+    return DUCKMOE_EINVAL;
+  PfArgs a = {};
+  a.E = n_routed;
+  a.K = top_k;
+  a.T = T;
+  a.ids = ids;
+  a.w = w;
+  a.status = status;
+  a.n_tiles = nullptr;
+  a.tiles = nullptr;
+  a.off = offsets;
+  a.tok = tokens;
+  a.wt = weights;
+  a.tok_entry = tok_entry;
+  return launch_plan(a, stream) == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
+}
+
+}  // extern "C"

@@ -83,6 +83,10 @@ _SIGNATURES = {
     "duckmoe_stack_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
     "duckmoe_moe_stack": ([ctypes.POINTER(LayerStruct), _I32, _P, _P, _P, _I32, ctypes.c_float,
                            _P, _P, _SZ, _P], ctypes.c_int),
+    "duckmoe_prefill_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
+    "duckmoe_moe_prefill": ([ctypes.POINTER(LayerStruct), _P, _P, _P, _I32, _P, _P, _SZ, _P],
+                            ctypes.c_int),
+    "duckmoe_prefill_plan": ([_P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
 }
 
 EXPORTS = tuple(_SIGNATURES)
@@ -310,6 +314,18 @@ class Layer:
         return torch.empty(self.workspace_bytes(T, n_shards), dtype=torch.uint8,
                            device=self.gu_body.device)
 
+    def prefill_workspace_bytes(self, T, routed=True):
+        n = lib().duckmoe_prefill_workspace_bytes(ctypes.byref(self.struct), T, int(routed))
+        if n == 0:
+            raise DuckMoeError(EINVAL, "duckmoe_prefill_workspace_bytes")
+        return n
+
+    def prefill_workspace(self, T, routed=True):
+        """A device workspace for a prefill call of T tokens (no initialisation)."""
+        import torch
+        return torch.empty(self.prefill_workspace_bytes(T, routed), dtype=torch.uint8,
+                           device=self.gu_body.device)
+
 
 def _layer_call(fname, layer, x, ids, w, out, n_shards, ws, stream):
     import torch
@@ -355,6 +371,47 @@ def expert_ffn(layer, e, x, out=None, n_shards=1, ws=None, stream=None):
                                   n_shards, _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "duckmoe_expert_ffn")
     return out
+
+
+def moe_prefill(layer, x, ids, w, out=None, ws=None, stream=None):
+    """The routed layer for many tokens (grouped by expert); ids None runs the
+    shared (or only) expert alone."""
+    import torch
+    T = x.shape[0]
+    _need_device(x, torch.float32, "x")
+    if ids is not None:
+        _need_device(ids, torch.int32, "ids")
+        _need_device(w, torch.float32, "w")
+        if tuple(ids.shape) != (T, layer.top_k) or tuple(w.shape) != (T, layer.top_k):
+            raise ValueError("ids and w must be [T, top_k]")
+    if out is None:
+        out = torch.empty((T, layer.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = layer.prefill_workspace(T, ids is not None)
+    rc = lib().duckmoe_moe_prefill(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w), T,
+                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "duckmoe_moe_prefill")
+    return out
+
+
+def prefill_plan(ids, w, n_routed, stream=None):
+    """Device per-expert token lists (test export) -> (offsets, tokens, weights,
+    tok_entry, status) as host numpy arrays."""
+    import torch
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.zeros(n_routed + 2, dtype=torch.int32, device=dev)
+    tokens = torch.full((T * (k + 1),), -1, dtype=torch.int32, device=dev)
+    weights = torch.zeros(T * (k + 1), dtype=torch.float32, device=dev)
+    tok_entry = torch.full((T, k + 1), -7, dtype=torch.int32, device=dev)
+    st = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    _check(lib().duckmoe_prefill_plan(_ptr(ids), _ptr(w), T, k, n_routed, _ptr(offsets),
+                                      _ptr(tokens), _ptr(weights), _ptr(tok_entry), _ptr(st),
+                                      _stream(stream)), "duckmoe_prefill_plan")
+    off = offsets.cpu().numpy()
+    n = int(off[-1])
+    return (off, tokens[:n].cpu().numpy(), weights[:n].cpu().numpy(),
+            tok_entry.cpu().numpy(), int(st.item()))
 
 
 def rms_normalize(x, eps=0.0, out=None, stream=None):

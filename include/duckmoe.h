@@ -18,7 +18,7 @@
  *  [route] chapter page "第 9 章 MTP1 dual-lane overlap", section 9.2
  *          "两条路线的判断": 8 routed experts per token (top_k = 8); the sets of
  *          two tokens barely overlap, so bsz 2 reads about twice the weights.
- *  [fp8]   same page, sections "真正埋下伏笔的是内存；R1 之后，问题第一次被改写"
+ *  [fp8]   memoir page, sections "真正埋下伏笔的是内存；R1 之后，问题第一次被改写"
  *          (the released checkpoints are fp8) and "先用 Qwen3 练级，再让
  *          Qwen3.5 充当高压试炼场" (the fp8 format uses 128 x 128 block scales).
  *  [lane]  chapter page "第 9 章 MTP1 dual-lane overlap", section 9.5
@@ -30,6 +30,9 @@
  *          an event recorded behind the work that produced its input; section
  *          9.6 "Rust overlap 接口": begin starts a lane's MoE forward and returns
  *          at once, finish waits for it and hands over the result.
+ *  [pf]    memoir page, section "限制条件": the fp9 prefill kernel is the part
+ *          still far from the machine's peak, and contexts were tested up to
+ *          2048 tokens; prefill is the same routed layer over many tokens.
  *  [f32]   ds4 glossary page "张量并行（Tensor Parallelism, TP）", section
  *          "形态一：Mac-to-Mac 张量并行（RDMA）": TP partial sums travel as f32.
  *
@@ -239,6 +242,58 @@ size_t duckmoe_stack_workspace_bytes(const duckmoe_layer *layers, int32_t n_laye
 int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float *x,
                       const int32_t *ids, const float *w, int32_t T, float eps, float *out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * [pf][route][fp9] Prefill: the routed layer of duckmoe_moe_layer for many
+ * tokens at once, with the tokens grouped by expert so that each selected
+ * expert's weights are streamed once per tile of up to 64 of its tokens, and
+ * the contractions run on the matrix cores (fp9 weights decoded to fp16,
+ * activations carried as scaled fp16 hi/lo pairs, f32 accumulation).
+ *   x [T][H], out [T][H]  float32 device, 16-byte aligned, 1 <= T <= 32768
+ *   ids, w [T][top_k]     int32 / float32 device; ids == NULL runs the shared
+ *                         (or, for n_routed = 0, the only) expert alone and
+ *                         ignores w
+ *   ws   device workspace of at least duckmoe_prefill_workspace_bytes(L, T,
+ *        ids != NULL) bytes, 256-byte aligned, needing no initialisation;
+ *        holds the per-expert token lists, the staged activations, h' and the
+ *        per-entry outputs (about T * (top_k + 1) * (4 H + 4 I) bytes)
+ * out_t = shared(x_t) + sum_i w[t][i] * expert_{ids[t][i]}(x_t); an id listed
+ * twice by one token adds its weights (status bit DUCKMOE_STATUS_DUP_ID), an
+ * id outside [0, n_routed) is skipped (DUCKMOE_STATUS_BAD_ID); the status word
+ * is read with duckmoe_status on ws.  Each output element is a sum in a fixed
+ * order: repeated calls give identical bits.
+ * Requirements beyond the layer's: n_routed <= 1024, top_k <= 32 when ids is
+ * given, T * roundup(H, 128) * 2 and T * (top_k + 1) * roundup(I, 128) * 2
+ * below 2^31 (DUCKMOE_ESHAPE).  DUCKMOE_EINVAL for T outside [1, 32768], null
+ * or misaligned pointers (w null with ids given); DUCKMOE_EWORKSPACE if
+ * ws_bytes is too small.  duckmoe_prefill_workspace_bytes returns 0 for an
+ * invalid layer or T.
+ */
+size_t duckmoe_prefill_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t routed);
+int duckmoe_moe_prefill(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                        const float *w, int32_t T, float *out, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * [pf] Test export: the per-expert token lists of a prefill call, written to
+ * caller buffers (device, asynchronous on stream).
+ *   ids, w [T][top_k] device (may be NULL when top_k == 0)
+ *   offsets   [n_routed + 2] int32: first entry of list p; list 0 is the
+ *             shared expert (every token, weight 1), list p >= 1 routed
+ *             expert p - 1; offsets[n_routed + 1] = number of entries
+ *   tokens    [T * (top_k + 1)] int32: entry -> token, ascending in a list
+ *   weights   [T * (top_k + 1)] float32: entry -> routing weight (summed in
+ *             id order for a repeated id)
+ *   tok_entry [T][top_k + 1] int32: token t's shared entry, then the entry of
+ *             ids[t][i] for the first position of each valid id, -1 for a
+ *             repeat or an id out of range
+ *   status    [1] int32: the status bits of the ids
+ * Errors: DUCKMOE_EINVAL for T outside [1, 32768], top_k outside [0, 32],
+ * n_routed outside [0, 1024] or null pointers.
+ */
+int duckmoe_prefill_plan(const int32_t *ids, const float *w, int32_t T, int32_t top_k,
+                         int32_t n_routed, int32_t *offsets, int32_t *tokens, float *weights,
+                         int32_t *tok_entry, int32_t *status, hipStream_t stream);
 
 /*
  * [pair] Asynchronous lanes.  A lane owns a stream, a workspace and two HIP

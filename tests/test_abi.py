@@ -114,6 +114,64 @@ def test_layer_argument_errors(L, fn):
     assert call_layer(L, mis, fn=fn) == E.EINVAL
 
 
+def prefill_ws_expected(H, I, E, k, T):
+    """Workspace of a prefill call, from the documented parts (256-byte aligned
+    each): header, list offsets, tile table, per-entry token/weight, tok_entry,
+    x hi/lo + scales, h' hi/lo + per-unit scales, y."""
+    a = lambda n: (n + 255) // 256 * 256
+    Hp, Ip = -(-H // 128) * 128, -(-I // 128) * 128
+    A = T * (k + 1)
+    tiles = -(-A // 64) + E + 1
+    parts = [256, (E + 2) * 4, tiles * 16, A * 4, A * 4, T * (k + 1) * 4, T * Hp * 2, T * Hp * 2,
+             T * 4, A * Ip * 2, A * Ip * 2, A * (Ip // 128) * 4, A * H * 4]
+    return sum(a(p) for p in parts)
+
+
+def test_prefill_workspace_bytes(L):
+    lay = fake_layer()
+    f = lambda T, routed=1, lay=lay: L.duckmoe_prefill_workspace_bytes(ctypes.byref(lay), T, routed)
+    for T in (1, 63, 2048, 32768):
+        assert f(T) == prefill_ws_expected(7168, 2048, 256, 8, T)
+    assert f(100, 0) == prefill_ws_expected(7168, 2048, 256, 0, 100)
+    odd = fake_layer(H=1040, I=336, E=24, k=8)
+    assert f(333, lay=odd) == prefill_ws_expected(1040, 336, 24, 8, 333)
+    assert f(0) == 0 and f(32769) == 0
+    assert f(1, lay=fake_layer(E=1025)) == 0          # more routed experts than the lists take
+    assert f(1, lay=fake_layer(k=33)) == 0            # top_k above 32 with ids
+    assert f(1, 0, lay=fake_layer(k=33)) > 0          # ... but fine without ids
+    assert L.duckmoe_prefill_workspace_bytes(None, 1, 1) == 0
+
+
+def test_prefill_errors(L):
+    E = dm.duckmoe
+    lay = fake_layer()
+
+    def c(lay=lay, x=FAKE, ids=FAKE, w=FAKE, T=4, out=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.duckmoe_moe_prefill(ctypes.byref(lay) if lay is not None else None, x, ids, w,
+                                     T, out, ws, wsb, None)
+    assert c(lay=None) == E.EINVAL
+    assert c(T=0) == E.EINVAL and c(T=32769) == E.EINVAL
+    assert c(w=None) == E.EINVAL
+    assert c(x=None) == E.EINVAL and c(out=None) == E.EINVAL and c(ws=None) == E.EINVAL
+    assert c(x=FAKE + 4) == E.EINVAL and c(out=FAKE + 8) == E.EINVAL
+    assert c(ws=FAKE + 16) == E.EINVAL
+    assert c(wsb=1000) == E.EWORKSPACE
+    assert c(ids=None, w=None, wsb=1000) == E.EWORKSPACE   # shared-only: w unused
+    for bad in (fake_layer(H=7160), fake_layer(I=2040), fake_layer(E=1025), fake_layer(k=33),
+                fake_layer(H=65536, I=16384)):
+        assert c(lay=bad) == E.ESHAPE
+    # x hi/lo above 2 GiB
+    assert c(lay=fake_layer(H=32768, I=2048), T=32768) == E.ESHAPE
+    mis = LayerStruct(7168, 2048, 256, 8, FAKE, FAKE + 1, FAKE, FAKE)
+    assert c(lay=mis) == E.EINVAL
+    p = L.duckmoe_prefill_plan
+    assert p(FAKE, FAKE, 0, 8, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.EINVAL
+    assert p(FAKE, FAKE, 4, 33, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.EINVAL
+    assert p(FAKE, FAKE, 4, 8, 1025, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.EINVAL
+    assert p(None, FAKE, 4, 8, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.EINVAL
+    assert p(FAKE, FAKE, 4, 8, 256, FAKE, FAKE, FAKE, None, FAKE, None) == E.EINVAL
+
+
 def test_expert_ffn_errors(L):
     E = dm.duckmoe
     lay = fake_layer()
