@@ -110,6 +110,12 @@ __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// The 16-bit result kept as 16 bits: widening it where it is used (not right
+// after the load) keeps the compiler from waiting for the load early.
+__device__ __forceinline__ uint16_t buf_load2h(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

@@ -41,7 +41,7 @@ __device__ __forceinline__ int mx_scale_exp(float m) {
 
 struct MxTile {     // one unit of one 16-row tile for one lane
   uint4 b0, b1;     // 2 x 16 body bytes (see the layout note)
-  uint32_t s0, s1;  // their sign bits (16 + 16)
+  uint16_t s0, s1;  // their sign bits (16 + 16)
 };
 
 // Load lane 4i + q's share: row `row` (= the tile's row i), columns
@@ -54,21 +54,26 @@ __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
   const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
   w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
   w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
-  w.s0 = buf_load2(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
-  w.s1 = buf_load2(rs, v1 ? row * (K / 8) + c / 8 + 8 : kOutOfRange);
+  w.s0 = buf_load2h(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
+  w.s1 = buf_load2h(rs, v1 ? row * (K / 8) + c / 8 + 8 : kOutOfRange);
 }
 
-// Move lane 4i + g's tile words to lane i + 16g.
+// Move lane 4i + g's tile words to lane i + 16g.  The empty volatile asm
+// consumes the loaded sign words here: without it the compiler may hoist the
+// arithmetic that merges them above an earlier barrier, which makes that
+// barrier wait for loads meant to stay in flight across it.
 __device__ __forceinline__ MxTile mx_to_mfma(const MxTile &w) {
   const int l = threadIdx.x & 63;
   const int src = 4 * ((4 * (l & 15) + (l >> 4)) & 63);  // byte address of lane 4(l % 16) + l / 16
   auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
+  uint16_t s0 = w.s0, s1 = w.s1;
+  asm volatile("" : "+v"(s0), "+v"(s1));
   MxTile o;
   o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
   o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
-  const uint32_t sg = mv(w.s0 | (w.s1 << 16));
-  o.s0 = sg & 0xFFFFu;
-  o.s1 = sg >> 16;
+  const uint32_t sg = mv((uint32_t)s0 | ((uint32_t)s1 << 16));
+  o.s0 = (uint16_t)(sg & 0xFFFFu);
+  o.s1 = (uint16_t)(sg >> 16);
   return o;
 }
 

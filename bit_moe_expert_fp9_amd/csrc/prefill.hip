@@ -56,13 +56,27 @@ namespace {
 constexpr int kPfTile = 64;                     // entries (tokens) per tile
 constexpr int kPfCols = kPfTile / 16;           // MFMA column tiles per tile
 constexpr int kPfWaves = 8;                     // waves per GEMM workgroup
-constexpr int kPfRT = 2;                        // 16-row tiles per wave and matrix
-constexpr int kPfRows = kPfWaves * kPfRT * 16;  // rows per GEMM task
+#ifndef DUCKMOE_PF_GU_RT
+#define DUCKMOE_PF_GU_RT 1          // gate/up: 16-row tiles per wave and matrix
+#endif
+#ifndef DUCKMOE_PF_GU_WG_PER_CU
+#define DUCKMOE_PF_GU_WG_PER_CU 2   // gate/up: resident workgroups per CU the registers must allow
+#endif
+#ifndef DUCKMOE_PF_DN_RT
+#define DUCKMOE_PF_DN_RT 2          // down: 16-row tiles per wave
+#endif
+#ifndef DUCKMOE_PF_DN_WG_PER_CU
+#define DUCKMOE_PF_DN_WG_PER_CU 1
+#endif
 constexpr int kPfPitch = 2 * kMxUnit + 16;      // LDS bytes per token row of a unit (padded)
 constexpr int kPfMaxTopK = 32;
 constexpr int kPfMaxRouted = 1024;
 constexpr int kPfMaxTokens = 32768;
-static_assert(kPfRT * 16 * 4 == kMxUnit, "4 waves cover one 128-row unit of h'");
+// rows of one GEMM task, and (gate/up) waves per 128-row unit of h'
+template <int RT>
+constexpr int pf_rows() { return kPfWaves * RT * 16; }
+template <int RT>
+constexpr int pf_wpu() { return kMxUnit / (RT * 16); }
 static_assert(kPfWaves * 64 * 4 == 2 * kPfTile * (2 * kMxUnit) / 16,
               "one workgroup stages a unit's hi/lo tile as 4 x 16 bytes per thread");
 
@@ -357,241 +371,259 @@ __device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t
   }
 }
 
-__device__ __forceinline__ int4 pf_tile(const PfArgs &a, int tile) {
-  const int4 t = a.tiles[tile];
-  return make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
-                   __builtin_amdgcn_readfirstlane(t.z), 0);
+// One task of a grouped GEMM: a tile (list, first entry, entries) times a
+// block of kPfRows output rows.  task >= ntask is "no task": no entries, every
+// load out of range.  Scalar fields are wave-uniform.
+struct PfTask {
+  int task, blk;
+  int e0, n, nct;
+  const uint8_t *body, *sign;  // the expert's planes of this matrix
+  uint32_t src[2];             // staging sources of this thread, unit 0 (bytes)
+  uint32_t hsrc;               // down: this thread's h' scale source, unit 0 (bytes)
+};
+
+template <bool GU>
+__device__ __forceinline__ PfTask pf_task(const PfArgs &a, int task, int NB, int ntask,
+                                          __amdgpu_buffer_rsrc_t rtok) {
+  PfTask t;
+  t.task = task;
+  const bool ok = task < ntask;
+  const int tile = ok ? task / NB : 0;
+  const int4 tl = a.tiles[tile];
+  t.blk = ok ? task - tile * NB : 0;
+  t.e0 = __builtin_amdgcn_readfirstlane(tl.y);
+  t.n = ok ? __builtin_amdgcn_readfirstlane(tl.z) : 0;
+  t.nct = (t.n + 15) / 16;
+  const int p = __builtin_amdgcn_readfirstlane(tl.x);
+  const size_t ex = p == 0 ? (size_t)a.E : (size_t)(p - 1);
+  const size_t mat = (size_t)a.I * a.H;
+  t.body = GU ? a.gu_body + ex * 2 * mat : a.dn_body + ex * mat;
+  t.sign = GU ? a.gu_sign + ex * 2 * (mat / 8) : a.dn_sign + ex * (mat / 8);
+  const uint32_t seg = threadIdx.x & 15;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int tt = (threadIdx.x >> 4) + 32 * q;
+    uint32_t row;
+    if (GU)  // the token's x row (gathered)
+      row = buf_load4(rtok, tt < t.n ? (uint32_t)(t.e0 + tt) * 4u : kOutOfRange) * (uint32_t)a.Hp;
+    else     // the entry's h' row
+      row = (uint32_t)(t.e0 + tt) * (uint32_t)a.Ip;
+    t.src[q] = tt < t.n ? (row + 8u * seg) * 2u : kOutOfRange;
+  }
+  const int nv = a.Ip / kMxUnit;
+  t.hsrc = (!GU && (int)threadIdx.x < t.n) ? (uint32_t)(t.e0 + threadIdx.x) * (uint32_t)nv * 4u
+                                           : kOutOfRange;
+  return t;
 }
 
-// Gate/up: task = (tile, block of kPfRows intermediate rows).
-__global__ __launch_bounds__(kPfWaves * 64) void k_pf_gate_up(const PfArgs a) {
-  constexpr int RT = kPfRT, NT = kPfCols;
+// Grouped GEMM over tasks (tile, block of kPfRows rows), the contraction in
+// 128-wide units.  GU: gate and up rows of the block against x (gathered by
+// token), epilogue h' = w * silu(gate) * up as scaled hi/lo rows.  !GU: down
+// rows against h' (the tile's entries are contiguous), each unit's h' scale
+// applied after its MFMAs, epilogue y[entry][row].
+//
+// Software pipeline over a flat stream of (task, unit) items: while item i is
+// computed, the weight tiles and the activation tile of item i + 1 (in the
+// next task after a task's last unit) are in flight; every load in the loop is
+// issued unconditionally (out-of-range offsets read zero) so the compiler's
+// wait counts stay exact and never drain the queue.  One barrier per unit.
+template <bool GU, int RT, int WGCU>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
+    WGCU * kPfWaves / 4, WGCU * kPfWaves / 4))) void k_pf_gemm(const PfArgs a) {
+  constexpr int NT = kPfCols, M = GU ? 2 : 1;
+  constexpr int kPfRows = pf_rows<RT>(), kPfWPU = pf_wpu<RT>();
+  static_assert(!GU || (kPfWPU * RT * 16 == kMxUnit && kPfWaves % kPfWPU == 0),
+                "gate/up waves tile the 128-row units of h'");
   __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * kPfTile * kPfPitch];
-  __shared__ float red[kPfWaves][kPfTile];
+  __shared__ float red[GU ? kPfWaves : 1][kPfTile];
+  __shared__ float lsc[2][GU ? 1 : kPfTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
   const int H = a.H, I = a.I;
-  const int NB = (I + kPfRows - 1) / kPfRows;
+  const int rows = GU ? I : H, Kd = GU ? H : I;
+  const int nu = (GU ? a.Hp : a.Ip) / kMxUnit, nv = a.Ip / kMxUnit;
+  const int NB = (rows + kPfRows - 1) / kPfRows;
   const int ntask = __builtin_amdgcn_readfirstlane(*a.n_tiles) * NB;
-  const int nu = a.Hp / kMxUnit, nv = a.Ip / kMxUnit;
-  const uint32_t mat = (uint32_t)I * (uint32_t)H;
-  const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.xh, (uint32_t)a.T * (uint32_t)a.Hp * 2u);
-  const __amdgpu_buffer_rsrc_t rxl = make_rsrc(a.xl, (uint32_t)a.T * (uint32_t)a.Hp * 2u);
+  const uint32_t mbytes = (GU ? 2u : 1u) * (uint32_t)I * (uint32_t)H;
+  const uint32_t act_bytes = GU ? (uint32_t)a.T * (uint32_t)a.Hp * 2u
+                                : (uint32_t)a.A * (uint32_t)a.Ip * 2u;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(GU ? (const void *)a.xh : (const void *)a.hh, act_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(GU ? (const void *)a.xl : (const void *)a.hl, act_bytes);
+  const __amdgpu_buffer_rsrc_t rtok = make_rsrc(a.tok, (uint32_t)a.A * 4u);
+  const __amdgpu_buffer_rsrc_t rhs = make_rsrc(a.hs, (uint32_t)a.A * (uint32_t)nv * 4u);
 
-  for (int task = pf_vid(); task < ntask; task += gridDim.x) {
-    const int tile = task / NB, blk = task - tile * NB;
-    const int4 tl = pf_tile(a, tile);
-    const int e0 = tl.y, n = tl.z, nct = (n + 15) / 16;
-    const int ex = tl.x == 0 ? a.E : tl.x - 1;
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)ex * 2 * mat, 2 * mat);
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(a.gu_sign + (size_t)ex * 2 * (mat / 8), 2 * (mat / 8));
-    uint32_t src[2];
+  int task = pf_vid();
+  if (task >= ntask) return;
+  PfTask cur = pf_task<GU>(a, task, NB, ntask, rtok);
+  PfTask nxt = pf_task<GU>(a, task + (int)gridDim.x, NB, ntask, rtok);
+
+  auto stage_src = [&](const PfTask &t, int u, uint32_t (&src)[2]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int tt = (threadIdx.x >> 4) + 32 * q;
-      src[q] = tt < n ? ((uint32_t)a.tok[e0 + tt] * (uint32_t)a.Hp + 8u * (threadIdx.x & 15)) * 2u
-                      : kOutOfRange;
+    for (int q = 0; q < 2; ++q)
+      src[q] = t.src[q] == kOutOfRange ? kOutOfRange : t.src[q] + (uint32_t)u * (2u * kMxUnit);
+  };
+  auto scale_src = [&](const PfTask &t, int u) {
+    return t.hsrc == kOutOfRange ? kOutOfRange : t.hsrc + (uint32_t)u * 4u;
+  };
+  auto load_w = [&](MxTile (&w)[RT][M], const PfTask &t, int u) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.body, mbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sign, mbytes / 8u);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = t.blk * kPfRows + wave * RT * 16 + 16 * r + (lane >> 2);
+      const bool rv = row < rows && t.n > 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        mx_load_w(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
+                  (uint32_t)(u * kMxUnit), rv);
     }
-    const int r0 = blk * kPfRows + wave * RT * 16;  // the wave's first row
-    auto load_w = [&](MxTile (&t)[RT][2], int u) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = r0 + 16 * r + (lane >> 2);
-        mx_load_w(t[r][0], rb, rs, (uint32_t)row, H, u * kMxUnit, row < I);
-        mx_load_w(t[r][1], rb, rs, (uint32_t)(I + row), H, u * kMxUnit, row < I);
-      }
-    };
+  };
 
-    f4v_t acc[RT][2][NT];
+  f4v_t acc[RT][M][NT];
+  auto zero = [&]() {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) acc[r][m][ct] = f4v_t{0, 0, 0, 0};
+  };
+  zero();
 
-    PfStage stg;
-    MxTile raw[RT][2];
-    pf_stage_load(stg, rxh, rxl, src, 0);
-    load_w(raw, 0);
+  PfStage stg;
+  MxTile raw[RT][M];
+  float scv = 0.0f;
+  {
+    uint32_t src[2];
+    stage_src(cur, 0, src);
+    pf_stage_load(stg, rh, rl, src, 0);
+    scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(cur, 0)));
+    load_w(raw, cur, 0);
     pf_stage_store(stg, lb[0]);
-    __syncthreads();
-    for (int u = 0; u < nu; ++u) {
-      const bool more = u + 1 < nu;
-      if (more) pf_stage_load(stg, rxh, rxl, src, (uint32_t)(u + 1) * kMxUnit * 2u);
-      MxTile wm[RT][2];
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
-      if (more) load_w(raw, u + 1);
-      pf_unit<RT, 2>(wm, lb[u & 1], nct, acc);
-      if (more) pf_stage_store(stg, lb[(u + 1) & 1]);
-      __syncthreads();
-    }
-
-    // epilogue: h' = w * silu(gate) * up, then per (entry, 128-row unit) scaled
-    // hi/lo rows; the unit is the 4 waves q0 .. q0 + 3
-    float mx[NT];
-    bool tv[NT];
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int tt = 16 * ct + j;
-      tv[ct] = tt < n;
-      const float xs = tv[ct] ? a.xinv[a.tok[e0 + tt]] : 0.0f;
-      const float wv = tv[ct] ? a.wt[e0 + tt] : 0.0f;
-      float m = 0.0f;
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gs = acc[r][0][ct][i] * xs, us = acc[r][1][ct][i] * xs;
-          const float hv = (wv == 0.0f) ? 0.0f : wv * (silu(gs) * us);
-          acc[r][0][ct][i] = hv;
-          m = fmaxf(m, fabsf(hv));
-        }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mx[ct] = m;
-      if (g == 0) red[wave][16 * ct + j] = m;
-    }
-    __syncthreads();
-    const int q0 = wave & ~3;
-    const int unit = (blk * kPfRows) / kMxUnit + (wave >> 2);
-    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int tt = 16 * ct + j;
-      const float M = fmaxf(fmaxf(red[q0][tt], red[q0 + 1][tt]), fmaxf(red[q0 + 2][tt], red[q0 + 3][tt]));
-      const int k = mx_scale_exp(M);
-      const float sc = ldexpf(1.0f, k);
-      if (tv[ct] && unit < nv) {
-        const size_t rowbase = (size_t)(e0 + tt) * a.Ip;
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const int row = r0 + 16 * r + 4 * g;
-          h4_t hi, lo;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = acc[r][0][ct][i] * sc;
-            hi[i] = (_Float16)v;
-            lo[i] = (_Float16)(v - (float)hi[i]);
-          }
-          *reinterpret_cast<h4_t *>(a.hh + rowbase + row) = hi;
-          *reinterpret_cast<h4_t *>(a.hl + rowbase + row) = lo;
-        }
-        if (wave == q0 && g == 0) a.hs[(size_t)(e0 + tt) * nv + unit] = ldexpf(1.0f, -k);
-      }
-      (void)mx[ct];
-    }
+    if (!GU && threadIdx.x < kPfTile) lsc[0][threadIdx.x] = scv;
     __syncthreads();
   }
-}
-
-// Down: task = (tile, block of kPfRows output rows); K = the intermediate
-// dimension in 128-wide units, each unit's h' scale applied after its MFMAs.
-__global__ __launch_bounds__(kPfWaves * 64) void k_pf_down(const PfArgs a) {
-  constexpr int RT = kPfRT, NT = kPfCols;
-  __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * kPfTile * kPfPitch];
-  __shared__ float lsc[2][kPfTile];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = lane & 15, g = lane >> 4;
-  const int H = a.H, I = a.I;
-  const int NB = (H + kPfRows - 1) / kPfRows;
-  const int ntask = __builtin_amdgcn_readfirstlane(*a.n_tiles) * NB;
-  const int nv = a.Ip / kMxUnit;
-  const uint32_t mat = (uint32_t)I * (uint32_t)H;
-  const __amdgpu_buffer_rsrc_t rhh = make_rsrc(a.hh, (uint32_t)a.A * (uint32_t)a.Ip * 2u);
-  const __amdgpu_buffer_rsrc_t rhl = make_rsrc(a.hl, (uint32_t)a.A * (uint32_t)a.Ip * 2u);
-
-  for (int task = pf_vid(); task < ntask; task += gridDim.x) {
-    const int tile = task / NB, blk = task - tile * NB;
-    const int4 tl = pf_tile(a, tile);
-    const int e0 = tl.y, n = tl.z, nct = (n + 15) / 16;
-    const int ex = tl.x == 0 ? a.E : tl.x - 1;
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)ex * mat, mat);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)ex * (mat / 8), mat / 8);
-    uint32_t src[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int tt = (threadIdx.x >> 4) + 32 * q;
-      src[q] = tt < n ? ((uint32_t)(e0 + tt) * (uint32_t)a.Ip + 8u * (threadIdx.x & 15)) * 2u
-                      : kOutOfRange;
-    }
-    const int r0 = blk * kPfRows + wave * RT * 16;
-    auto load_w = [&](MxTile (&t)[RT][1], int u) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = r0 + 16 * r + (lane >> 2);
-        mx_load_w(t[r][0], rb, rs, (uint32_t)row, I, u * kMxUnit, row < H);
-      }
-    };
-    auto load_sc = [&](int u) {
-      const int tt = threadIdx.x;
-      return (tt < n) ? a.hs[(size_t)(e0 + tt) * nv + u] : 0.0f;
-    };
-
-    f4v_t acc[RT][NT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) acc[r][ct] = f4v_t{0, 0, 0, 0};
-
-    PfStage stg;
-    MxTile raw[RT][1];
-    float scv = 0.0f;
-    pf_stage_load(stg, rhh, rhl, src, 0);
-    if (threadIdx.x < kPfTile) scv = load_sc(0);
-    load_w(raw, 0);
-    pf_stage_store(stg, lb[0]);
-    if (threadIdx.x < kPfTile) lsc[0][threadIdx.x] = scv;
-    __syncthreads();
-    for (int u = 0; u < nv; ++u) {
-      const bool more = u + 1 < nv;
-      if (more) {
-        pf_stage_load(stg, rhh, rhl, src, (uint32_t)(u + 1) * kMxUnit * 2u);
-        if (threadIdx.x < kPfTile) scv = load_sc(u + 1);
-      }
-      MxTile wm[RT][1];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) wm[r][0] = mx_to_mfma(raw[r][0]);
-      if (more) load_w(raw, u + 1);
-      f4v_t tmp[RT][1][NT];
+  int par = 0;
+  for (;;) {
+    for (int u = 0; u < nu; ++u) {
+      const bool last = u + 1 == nu;
+      const PfTask &nt = last ? nxt : cur;
+      const int un = last ? 0 : u + 1;
+      uint32_t src[2];
+      stage_src(nt, un, src);
+      pf_stage_load(stg, rh, rl, src, 0);
+      if (!GU) scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(nt, un)));
+      MxTile wm[RT][M];
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
-      pf_unit<RT, 1>(wm, lb[u & 1], nct, tmp);
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
+      load_w(raw, nt, un);
+      if (GU) {
+        pf_unit<RT, M>(wm, lb[par], cur.nct, acc);
+      } else {
+        f4v_t tmp[RT][M][NT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
+        pf_unit<RT, M>(wm, lb[par], cur.nct, tmp);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          if (ct < cur.nct) {
+            const float sc = lsc[par][16 * ct + j];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) acc[r][0][ct] += tmp[r][0][ct] * sc;
+          }
+        }
+      }
+      pf_stage_store(stg, lb[par ^ 1]);
+      if (!GU && threadIdx.x < kPfTile) lsc[par ^ 1][threadIdx.x] = scv;
+      __syncthreads();
+      par ^= 1;
+    }
+
+    const int r0 = cur.blk * kPfRows + wave * RT * 16;  // the wave's first row
+    if (GU) {
+      // h' = w * silu(gate) * up; per (entry, 128-row unit) scaled hi/lo rows,
+      // the unit being the 4 waves q0 .. q0 + 3
+      const __amdgpu_buffer_rsrc_t rxi = make_rsrc(a.xinv, (uint32_t)a.T * 4u);
+      const __amdgpu_buffer_rsrc_t rwt = make_rsrc(a.wt, (uint32_t)a.A * 4u);
+      bool tv[NT];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        if (ct < nct) {
-          const float s = lsc[u & 1][16 * ct + j];
+        const int tt = 16 * ct + j;
+        tv[ct] = tt < cur.n;
+        const uint32_t tk = buf_load4(rtok, tv[ct] ? (uint32_t)(cur.e0 + tt) * 4u : kOutOfRange);
+        const float xs = __builtin_bit_cast(float, buf_load4(rxi, tv[ct] ? tk * 4u : kOutOfRange));
+        const float wv = __builtin_bit_cast(
+            float, buf_load4(rwt, tv[ct] ? (uint32_t)(cur.e0 + tt) * 4u : kOutOfRange));
+        float m = 0.0f;
 #pragma unroll
-          for (int r = 0; r < RT; ++r) acc[r][ct] += tmp[r][0][ct] * s;
-        }
-      }
-      if (more) {
-        pf_stage_store(stg, lb[(u + 1) & 1]);
-        if (threadIdx.x < kPfTile) lsc[(u + 1) & 1][threadIdx.x] = scv;
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gs = acc[r][0][ct][i] * xs, us = acc[r][M - 1][ct][i] * xs;
+            const float hv = (wv == 0.0f) ? 0.0f : wv * (silu(gs) * us);
+            acc[r][0][ct][i] = hv;
+            m = fmaxf(m, fabsf(hv));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (g == 0) red[wave][tt] = m;
       }
       __syncthreads();
-    }
+      const int q0 = wave - wave % kPfWPU;
+      const int unit = (cur.blk * kPfRows) / kMxUnit + wave / kPfWPU;
+      typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int tt = 16 * ct + j;
-      if (tt < n) {
+      for (int ct = 0; ct < NT; ++ct) {
+        const int tt = 16 * ct + j;
+        float mx = red[q0][tt];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const int row = r0 + 16 * r + 4 * g;
-          if (row < H)
-            *reinterpret_cast<float4 *>(a.y + (size_t)(e0 + tt) * H + row) =
-                make_float4(acc[r][ct][0], acc[r][ct][1], acc[r][ct][2], acc[r][ct][3]);
+        for (int q = 1; q < kPfWPU; ++q) mx = fmaxf(mx, red[q0 + q][tt]);
+        const int k = mx_scale_exp(mx);
+        const float sc = ldexpf(1.0f, k);
+        if (tv[ct] && unit < nv) {
+          const size_t rowbase = (size_t)(cur.e0 + tt) * a.Ip;
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const int row = r0 + 16 * r + 4 * g;
+            h4_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = acc[r][0][ct][i] * sc;
+              hi[i] = (_Float16)v;
+              lo[i] = (_Float16)(v - (float)hi[i]);
+            }
+            *reinterpret_cast<h4_t *>(a.hh + rowbase + row) = hi;
+            *reinterpret_cast<h4_t *>(a.hl + rowbase + row) = lo;
+          }
+          if (wave == q0 && g == 0) a.hs[(size_t)(cur.e0 + tt) * nv + unit] = ldexpf(1.0f, -k);
+        }
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int tt = 16 * ct + j;
+        if (tt < cur.n) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const int row = r0 + 16 * r + 4 * g;
+            if (row < H)
+              *reinterpret_cast<float4 *>(a.y + (size_t)(cur.e0 + tt) * H + row) =
+                  make_float4(acc[r][0][ct][0], acc[r][0][ct][1], acc[r][0][ct][2],
+                              acc[r][0][ct][3]);
+          }
         }
       }
     }
+    zero();
+    if (nxt.task >= ntask) break;
+    cur = nxt;
+    nxt = pf_task<GU>(a, cur.task + (int)gridDim.x, NB, ntask, rtok);
   }
 }
 
@@ -665,9 +697,6 @@ int pf_check(const duckmoe_layer *L, int T, bool routed) {
   return DUCKMOE_OK;
 }
 
-#ifndef DUCKMOE_PF_WAVES_PER_CU
-#define DUCKMOE_PF_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
-#endif
 
 hipError_t launch_plan(const PfArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(k_pf_count, dim3(a.E + 1), dim3(256), 0, st, a);
@@ -735,15 +764,18 @@ int duckmoe_moe_prefill(const duckmoe_layer *L, const float *x, const int32_t *i
   if (launch_plan(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   hipLaunchKernelGGL(k_pf_xprep, dim3(T), dim3(256), 0, stream, a);
   const int threads = kPfWaves * 64;
+  constexpr int RG = DUCKMOE_PF_GU_RT, RD = DUCKMOE_PF_DN_RT;
+  constexpr int CG = DUCKMOE_PF_GU_WG_PER_CU, CD = DUCKMOE_PF_DN_WG_PER_CU;
+  const auto kgu = k_pf_gemm<true, RG, CG>;
+  const auto kdn = k_pf_gemm<false, RD, CD>;
   int g1 = 0, g2 = 0;
-  const int NBi = (a.I + kPfRows - 1) / kPfRows, NBh = (a.H + kPfRows - 1) / kPfRows;
-  if (persistent_grid(k_pf_gate_up, threads, DUCKMOE_PF_WAVES_PER_CU, l.max_tiles * NBi, g1) !=
-          hipSuccess ||
-      persistent_grid(k_pf_down, threads, DUCKMOE_PF_WAVES_PER_CU, l.max_tiles * NBh, g2) !=
-          hipSuccess)
+  const int NBi = (a.I + pf_rows<RG>() - 1) / pf_rows<RG>();
+  const int NBh = (a.H + pf_rows<RD>() - 1) / pf_rows<RD>();
+  if (persistent_grid(kgu, threads, CG * kPfWaves, l.max_tiles * NBi, g1) != hipSuccess ||
+      persistent_grid(kdn, threads, CD * kPfWaves, l.max_tiles * NBh, g2) != hipSuccess)
     return DUCKMOE_EHIP;
-  hipLaunchKernelGGL(k_pf_gate_up, dim3(g1), dim3(threads), 0, stream, a);
-  hipLaunchKernelGGL(k_pf_down, dim3(g2), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(kgu, dim3(g1), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(kdn, dim3(g2), dim3(threads), 0, stream, a);
   const size_t n4 = (size_t)T * (a.H / 4);
   hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
