@@ -395,6 +395,32 @@ def test_full_layer_bsz8_max_ids(torch_dev, v3_layer):
     check_close(got, oracle.moe_layer(ox, x, ids, w, E3), "layer bsz8")
 
 
+def test_full_layer_prefill_2048(torch_dev, v3_layer):
+    """The prefill workload: 2048 tokens through the 257-expert layer (every
+    expert selected, the shared one in 32 tiles); sampled tokens against the
+    oracle, and the whole output against the decode path on 8-token slices."""
+    torch = torch_dev
+    lay, ox = v3_layer
+    T = 2048
+    x = synth.activations(SEED, 7, 0, 0, T, H3)
+    ids, w = synth.routing(SEED, 7, 0, 0, T, E3, K3)
+    say("full layer prefill T = 2048")
+    xd, idd, wd = to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w)
+    ws = lay.prefill_workspace(T)
+    got = dm.moe_prefill(lay, xd, idd, wd, ws=ws).cpu().numpy()
+    assert dm.status(ws) == 0
+    toks = [0, 1337]
+    ox.prefetch(list(ids[toks].ravel()) + [E3])
+    ref = oracle.moe_layer(ox, x[toks], ids[toks], w[toks], E3)
+    for i, t in enumerate(toks):
+        check_close(got[t], ref[i], "prefill T=2048 token %d" % t)
+    say("prefill T = 2048 against the decode path, 8 tokens at a time")
+    for t0 in range(0, T, 8):
+        dec = dm.moe_layer(lay, xd[t0:t0 + 8], idd[t0:t0 + 8], wd[t0:t0 + 8]).cpu().numpy()
+        for t in range(8):
+            check_close(got[t0 + t], dec[t], "prefill vs decode token %d" % (t0 + t))
+
+
 def test_read_probe_runs(torch_dev):
     """The calibration read touches only its buffer and leaves the sink alone."""
     torch = torch_dev
