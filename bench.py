@@ -34,8 +34,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "9db6a812908ce59edfc255146ee7fc20d06badc8410f3ae4bc28f802d0a913fa",
-    "bytes_per_launch": 297760841,
+    "sources_sha256": "7f02aa3dd818b8fa06ae72652577fa307b07bc3df15e0b0f5787efc9206c4e20",
+    "bytes_per_launch": 297760148,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
                   "bit_moe_expert_fp9_amd/csrc/mfma_device.h", "bit_moe_expert_fp9_amd/csrc/host_util.h")

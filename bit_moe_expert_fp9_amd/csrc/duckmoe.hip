@@ -1297,10 +1297,12 @@ size_t ws_need(const duckmoe_layer *L, int T, bool single) {
   return T >= DUCKMOE_MX_MIN_T ? mx_layout(L, T, single, base).end : base;
 }
 
-// rows per down block: more rows share each h' load, fewer keep registers in check
+// rows per down block: more rows share each h' load, fewer give more blocks (waves
+// in flight) and keep registers in check; 7 measured best at bsz 1 and 2
+// (1024 blocks of the 7168 output rows)
 template <int T>
 constexpr int down_rows() {
-  return T == 1 ? DUCKMOE_DN_ROWS : (T == 2 ? 2 * DUCKMOE_DN_ROWS : (T <= 4 ? DUCKMOE_DN_ROWS : 2));
+  return T <= 4 ? DUCKMOE_DN_ROWS : 2;
 }
 
 template <int TG>
