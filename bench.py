@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=4,
+    p.add_argument("--cpu-tokens", type=int, default=16,
                    help="tokens (bsz 1 steps) the oracle times for the CPU baseline")
     p.add_argument("--bsz2", type=int, default=1, help="also time bsz 2 (0 to skip)")
     p.add_argument("--stack", action="store_true",
