@@ -678,8 +678,10 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 // lo = fp16((v - hi) * 2^11), after scaling every token row (x) or (slot,
 // token) row (h') by a power of two that puts its largest magnitude in
 // [2^13, 2^14), so neither part overflows and the pair carries about 22 bits.
-// Two MFMAs (A*hi, A*lo) per step, recombined in f32 as acc_hi + acc_lo * 2^-11
-// and unscaled exactly.
+// With at most 8 tokens both parts fit one B operand: column j < 8 holds the hi
+// part of token j and column 8 + j its lo part, so one MFMA per step gives
+// both products, recombined in f32 as acc[j] + acc[8 + j] * 2^-11 and unscaled
+// exactly.
 //
 // Lane layout (checked on gfx950): A[i][k] is in lane i + 16 * (k / 8), element
 // k % 8; B[k][j] in lane j + 16 * (k / 8), element k % 8; the accumulator
@@ -694,13 +696,16 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 constexpr int kMxGroups = 8;   // slot groups of the down pass (partials per row)
 constexpr float kLoScale = 2048.0f;
 
-// The hi/lo parts are stored as [column / 8][token][8]: the 8 columns a lane
-// takes for one MFMA step are 16 contiguous bytes, and the lanes of one lane
-// group (consecutive tokens) read consecutive 16-byte pieces.
+// The hi/lo parts are stored as [column / 8][part][token][8] (part 0 hi, 1 lo):
+// the 8 columns a lane takes for one MFMA step are 16 contiguous bytes, and the
+// lanes of one lane group (hi of tokens 0 .. T-1, then their lo) read 16-byte
+// pieces that are contiguous for T = 8.
+static_assert(kMaxT <= 8, "hi and lo of every token share one 16-column B operand");
+static_assert(kMaxIds + 1 <= 128, "the down pass keeps the slots' experts in two lane words");
 struct MxArgs {
-  _Float16 *xh, *xl;  // [Hp/8][T][8] scaled activations, hi and lo (zero padded)
+  _Float16 *xb;       // [Hp/8][2][T][8] scaled activations, hi and lo (zero padded)
   float *xinv;        // [T] 2^-k of each token's scale
-  _Float16 *hh, *hl;  // [slots][Ip/8][T][8] scaled h'
+  _Float16 *hb;       // [slots][Ip/8][2][T][8] scaled h'
   float *hinv;        // [slots][T]
   float *part;        // [kMxGroups][T][H] down partials
   int Hp, Ip;         // H, I rounded up to whole units
@@ -712,36 +717,63 @@ __device__ __forceinline__ void mx_split(float v, _Float16 &hi, _Float16 &lo) {
 }
 
 // Split one token's row of n floats (optionally divided by r first) into scaled
-// hi/lo parts of width np (zeros past n), stored as [np/8][T][8] at token t;
-// returns 2^-k.  One workgroup of 256 threads.
-__device__ float mx_prep_row(const float *src, int n, int np, float r, _Float16 *hi,
-                             _Float16 *lo, int T, int t, float *red) {
-  // n and np are multiples of 4 (of 16 and 128): float4 loads, 4 per trip
+// hi/lo parts of width np (zeros past n), stored as [np/8][2][T][8] at token t;
+// returns 2^-k.  One workgroup of 256 threads.  Rows of up to 8192 floats are
+// read once, into registers (all loads in flight together); longer rows are
+// read twice.
+constexpr int kPrepRegs = 8;  // float4s per thread held in registers
+
+__device__ __forceinline__ void mx_prep_store(float4 v, float r, float sc, int i, _Float16 *dst,
+                                              int T, int t) {
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  _Float16 h[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mx_split((e[q] / r) * sc, h[q], l[q]);
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  const size_t o = ((size_t)(i >> 1) * 2 * T + t) * 8 + 4 * (i & 1);  // columns 4i .. 4i + 3
+  *reinterpret_cast<h4_t *>(dst + o) = h4_t{h[0], h[1], h[2], h[3]};
+  *reinterpret_cast<h4_t *>(dst + o + (size_t)T * 8) = h4_t{l[0], l[1], l[2], l[3]};
+}
+
+__device__ __forceinline__ float absmax4(float4 v, float r) {
+  return fmaxf(fmaxf(fabsf(v.x / r), fabsf(v.y / r)), fmaxf(fabsf(v.z / r), fabsf(v.w / r)));
+}
+
+__device__ float mx_prep_row(const float *src, int n, int np, float r, _Float16 *dst, int T,
+                             int t, float *red) {
+  // n and np are multiples of 4 (of 16 and 128): float4 loads
   const float4 *s4 = reinterpret_cast<const float4 *>(src);
   const int n4 = n / 4, np4 = np / 4;
+  const bool in_regs = np4 <= kPrepRegs * 256;
+  float4 v[kPrepRegs];
   float m = 0.0f;
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kPrepRegs; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      v[q] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < kPrepRegs; ++q) m = fmaxf(m, absmax4(v[q], r));
+  } else {
 #pragma unroll 4
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 v = s4[i];
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x / r), fabsf(v.y / r)), fmaxf(fabsf(v.z / r), fabsf(v.w / r))));
+    for (int i = threadIdx.x; i < n4; i += 256) m = fmaxf(m, absmax4(s4[i], r));
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   const int k = mx_scale_exp(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
   const float sc = ldexpf(1.0f, k);
-#pragma unroll 4
-  for (int i = threadIdx.x; i < np4; i += 256) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < n4) v = s4[i];
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    _Float16 h[4], l[4];
+  if (in_regs) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mx_split((e[q] / r) * sc, h[q], l[q]);
-    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-    const size_t o = ((size_t)(i >> 1) * T + t) * 8 + 4 * (i & 1);  // columns 4i .. 4i + 3
-    *reinterpret_cast<h4_t *>(hi + o) = h4_t{h[0], h[1], h[2], h[3]};
-    *reinterpret_cast<h4_t *>(lo + o) = h4_t{l[0], l[1], l[2], l[3]};
+    for (int q = 0; q < kPrepRegs; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      if (i < np4) mx_prep_store(v[q], r, sc, i, dst, T, t);
+    }
+  } else {
+#pragma unroll 4
+    for (int i = threadIdx.x; i < np4; i += 256)
+      mx_prep_store(i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f), r, sc, i, dst, T, t);
   }
   return ldexpf(1.0f, -k);
 }
@@ -760,7 +792,7 @@ __global__ __launch_bounds__(256) void k_mx_xprep(const LayerArgs a, const MxArg
     __syncthreads();
     r = rms_divisor(part, a.H, a.in_eps);
   }
-  const float inv = mx_prep_row(row, a.H, m.Hp, r, m.xh, m.xl, a.T, t, red);
+  const float inv = mx_prep_row(row, a.H, m.Hp, r, m.xb, a.T, t, red);
   if (threadIdx.x == 0) m.xinv[t] = inv;
 }
 
@@ -772,33 +804,34 @@ __global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArg
   const int slot = blockIdx.x / a.T, t = blockIdx.x - slot * a.T;
   if (slot >= __builtin_amdgcn_readfirstlane(plan[0])) return;
   const size_t rowi = (size_t)slot * a.T + t;
-  const size_t blk = (size_t)slot * a.T * m.Ip;  // the slot's [Ip/8][T][8] block
-  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hh + blk, m.hl + blk,
-                                a.T, t, red);
+  const size_t blk = (size_t)slot * 2 * a.T * m.Ip;  // the slot's [Ip/8][2][T][8] block
+  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hb + blk, a.T, t, red);
   if (threadIdx.x == 0) m.hinv[rowi] = inv;
 }
 
-struct MxAct {      // the lane's 32 activations of one unit, hi and lo
-  uint4 h[4], l[4];
+struct MxAct {      // the lane's 32 B values of one unit (hi or lo of one token)
+  uint4 v[4];
 };
 
-// B for lane (token j, group g): columns c0 + 16g + 8s (s = 0, 1) and
-// c0 + 64 + 16g + 8(s - 2) (s = 2, 3), from a [cols/8][T][8] block at byte base.
-__device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t rh,
-                                          __amdgpu_buffer_rsrc_t rl, uint32_t base, uint32_t c0,
-                                          int T, bool v) {
+// B for lane (column j, group g): part j / 8 of token j % 8, columns
+// c0 + 16g + 8s (s = 0, 1) and c0 + 64 + 16g + 8(s - 2) (s = 2, 3), from a
+// [cols/8][2][T][8] block at byte base; zeros for tokens at or past T, and
+// everywhere when live is false (the loads are issued either way).
+__device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t r, uint32_t base,
+                                          uint32_t c0, int T, bool live) {
   const int j = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const uint32_t row = (uint32_t)(j >> 3) * (uint32_t)T + (uint32_t)(j & 7);
+  const bool v = live && (j & 7) < T;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const uint32_t kb = (c0 + 16 * g) / 8 + (s & 1) + 8 * (s >> 1);
-    const uint32_t o = base + (kb * (uint32_t)T + j) * 16u;
-    b.h[s] = buf_load16(rh, v ? o : kOutOfRange);
-    b.l[s] = buf_load16(rl, v ? o : kOutOfRange);
+    const uint32_t o = base + (kb * 2u * (uint32_t)T + row) * 16u;
+    b.v[s] = buf_load16(r, v ? o : kOutOfRange);
   }
 }
 
-// acc_hi += A * B_hi, acc_lo += A * B_lo over the unit's 4 steps
-__device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &ah, f4v_t &al) {
+// acc += A * B over the unit's 4 steps (columns j: hi of token j, 8 + j: its lo)
+__device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &acc) {
   const MxTile w = mx_to_mfma(wl);
   h2_t d[16];
   fp9_decode16(w.b0, w.s0, d);
@@ -808,8 +841,7 @@ __device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &
     const half8_t A = __builtin_bit_cast(half8_t, make_uint4(
         __builtin_bit_cast(uint32_t, d[4 * s]), __builtin_bit_cast(uint32_t, d[4 * s + 1]),
         __builtin_bit_cast(uint32_t, d[4 * s + 2]), __builtin_bit_cast(uint32_t, d[4 * s + 3])));
-    ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, b.h[s]), ah, 0, 0, 0);
-    al = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, b.l[s]), al, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, b.v[s]), acc, 0, 0, 0);
   }
 }
 
@@ -818,7 +850,11 @@ __device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &
 // of the task, or one empty item (u = -1) when the wave has no unit in it, so
 // that every wave closes every task exactly once (the close has a barrier).
 // The loads of the next item, possibly in the next task, are issued before the
-// current one is computed.
+// current one is computed.  Every item issues the same loads, an empty item or
+// one past the last task with out-of-range offsets (they read zeros and touch
+// no memory): with a branch around them the compiler could not know how many
+// loads are in flight behind the current item's, and its waits would drain the
+// next item's loads as well.
 struct MxItem {
   int task;
   int u;  // unit index, -1 for the empty item
@@ -836,7 +872,7 @@ struct GuMxBuf {
 
 template <int WA, int RT>
 __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const MxArgs m) {
-  __shared__ f4v_t red[2][WA][RT * 4][64];
+  __shared__ f4v_t red[2][WA][RT * 2][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H, I = a.I, T = a.T;
@@ -854,50 +890,56 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   };
   const int j = lane & 15, g = lane >> 4;
   const uint32_t mat = (uint32_t)I * (uint32_t)H;
-  const __amdgpu_buffer_rsrc_t rxh = make_rsrc(m.xh, (uint32_t)(T * m.Hp) * 2u);
-  const __amdgpu_buffer_rsrc_t rxl = make_rsrc(m.xl, (uint32_t)(T * m.Hp) * 2u);
-  const bool jv = j < T;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(m.xb, (uint32_t)(2 * T * m.Hp) * 2u);
+  const bool jv = j < T;  // lanes that finish token j (j < 8)
+  // token j's unscale factor, loaded once: a load in the task epilogue would
+  // wait for every load issued before it, the next item's included
+  float xs = __builtin_bit_cast(float, buf_load4(make_rsrc(m.xinv, (uint32_t)T * 4u),
+                                                 jv ? (uint32_t)j * 4u : kOutOfRange));
 
   auto issue = [&](GuMxBuf<WA, RT> &bf, MxItem it) {
-    if (it.u < 0) return;
-    const int slot = it.task / NB, r0 = (it.task - slot * NB) * 16 * RT;
+    const bool live = it.u >= 0 && it.task < ntask;
+    const int task = live ? it.task : 0, u = live ? it.u : 0;
+    const int slot = task / NB, r0 = (task - slot * NB) * 16 * RT;
     const int e = plan_expert(plan, slot);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
-    const uint32_t c0 = (uint32_t)(it.u * kMxUnit);
+    const uint32_t c0 = (uint32_t)(u * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = r0 + 16 * t + (lane >> 2);
-      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c0, row < I);
-      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, row < I);
+      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c0, live && row < I);
+      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, live && row < I);
     }
-    mx_load_b(bf.b, rxh, rxl, 0u, c0, T, jv);
+    mx_load_b(bf.b, rx, 0u, c0, T, live);
   };
 
-  f4v_t acc[RT][4];
+  f4v_t acc[RT][2];  // gate, up
   auto zero = [&]() {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[t][f] = f4v_t{0, 0, 0, 0};
+      for (int f = 0; f < 2; ++f) acc[t][f] = f4v_t{0, 0, 0, 0};
   };
   zero();
   int parity = 0;
 
+  // An empty item's tiles are zeros and add nothing; computing them anyway
+  // consumes every load, so no register of the item is still being written
+  // when the next issue reuses it.
   auto consume = [&](const GuMxBuf<WA, RT> &bf, MxItem it) {
-    if (it.u >= 0) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        mx_mma(bf.g[t], bf.b, acc[t][0], acc[t][1]);
-        mx_mma(bf.u[t], bf.b, acc[t][2], acc[t][3]);
-      }
+    for (int t = 0; t < RT; ++t) {
+      mx_mma(bf.g[t], bf.b, acc[t][0]);
+      mx_mma(bf.u[t], bf.b, acc[t][1]);
     }
-    if (it.u >= 0 && it.u + WA < nu) return;
-    // close the task: partials to LDS, wave 0 reduces and writes h'
+    if (it.task >= ntask || (it.u >= 0 && it.u + WA < nu)) return;
+    // close the task: partials to LDS, wave 0 reduces and writes h' (lane j < 8
+    // adds the hi sums of its own column and the lo sums of column 8 + j)
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) red[parity][wave][4 * t + f][lane] = acc[t][f];
+      for (int f = 0; f < 2; ++f) red[parity][wave][2 * t + f][lane] = acc[t][f];
     zero();
     __syncthreads();
     if (wave == 0) {
@@ -907,18 +949,17 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
         const float w_t = plan_weight(plan, a, slot, t);
         if (t == j) wt = w_t;
       }
-      const float xs = jv ? m.xinv[j] : 0.0f;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         f4v_t G = {0, 0, 0, 0}, Gl = G, U = G, Ul = G;
-#pragma unroll
-        for (int w = 0; w < WA; ++w) {
-          G += red[parity][w][4 * t + 0][lane];
-          Gl += red[parity][w][4 * t + 1][lane];
-          U += red[parity][w][4 * t + 2][lane];
-          Ul += red[parity][w][4 * t + 3][lane];
-        }
         if (jv) {
+#pragma unroll
+          for (int w = 0; w < WA; ++w) {
+            G += red[parity][w][2 * t + 0][lane];
+            Gl += red[parity][w][2 * t + 0][lane + 8];
+            U += red[parity][w][2 * t + 1][lane];
+            Ul += red[parity][w][2 * t + 1][lane + 8];
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = r0 + 16 * t + 4 * g + r;
@@ -935,23 +976,28 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
 
   GuMxBuf<WA, RT> b0, b1;
   MxItem i0 = first(), i1;
-  if (i0.task < ntask) issue(b0, i0);
+  issue(b0, i0);
+  asm volatile("" : "+v"(xs));  // xs arrives here, the first item stays in flight
+  // Items go in pairs; the second of the last pair may lie past the last task
+  // (zeros, no close).  No exit between the two halves: a path that leaves with
+  // one buffer's loads unconsumed would make the compiler's waits at the loop
+  // head assume those loads may still be writing their registers.
   while (i0.task < ntask) {
     i1 = next(i0);
-    if (i1.task < ntask) issue(b1, i1);
+    issue(b1, i1);
     consume(b0, i0);
-    if (i1.task >= ntask) break;
     i0 = next(i1);
-    if (i0.task < ntask) issue(b0, i0);
+    issue(b0, i0);
     consume(b1, i1);
   }
 }
 
 // Down: a workgroup takes tasks (block of 16 * RT rows of H, slot group q) and
 // splits the (slot, unit of I) items of the group's slots over its waves; each
-// item's hi/lo accumulators are unscaled into the wave's running sum; the
-// waves' sums meet in LDS and wave 0 writes the group's partial for the block's
-// rows.  The groups' partials are added by k_mx_reduce in a fixed order.
+// item's accumulator is unscaled into the wave's running sum (column j by the
+// token's scale, column 8 + j by that scale times 2^-11); the waves' sums meet
+// in LDS and wave 0 writes the group's partial for the block's rows, adding
+// columns j and 8 + j.  The groups' partials are added by k_mx_reduce in a fixed order.
 template <int WA, int RT>
 struct DnMxBuf {
   MxTile w[RT];
@@ -968,15 +1014,21 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H, I = a.I, T = a.T;
   const int S = __builtin_amdgcn_readfirstlane(plan[0]);
+  // lane l holds the expert of slot l (slots past 64 from a second word): a
+  // load per item would be a wait for every load in flight before it
+  const int eslot_lo = plan[1 + lane];
+  const int eslot_hi = plan[1 + min(64 + lane, kMaxIds)];
   const int nv = m.Ip / kMxUnit;
   const int NBH = (H + 16 * RT - 1) / (16 * RT);
   const int ntask = NBH * kMxGroups;
   const int j = lane & 15, g = lane >> 4;
-  const bool jv = j < T;
+  const bool jv = j < T;             // lanes that finish token j (j < 8)
+  const bool bv = (j & 7) < T;       // lanes whose column holds a token's part
+  const float part_scale = j < 8 ? 1.0f : 1.0f / kLoScale;
   const uint32_t mat = (uint32_t)I * (uint32_t)H;
   const int max_slots = a.ids != nullptr ? T * a.top_k + 1 : 1;
-  const __amdgpu_buffer_rsrc_t rhh = make_rsrc(m.hh, (uint32_t)(max_slots * T * m.Ip) * 2u);
-  const __amdgpu_buffer_rsrc_t rhl = make_rsrc(m.hl, (uint32_t)(max_slots * T * m.Ip) * 2u);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(m.hb, (uint32_t)(max_slots * 2 * T * m.Ip) * 2u);
+  const __amdgpu_buffer_rsrc_t rhs = make_rsrc(m.hinv, (uint32_t)(max_slots * T) * 4u);
   // items of the task's group: (slot q + s * G, unit v) for s < ns_q, v < nv
   auto n_items = [&](int task) {
     const int q = task / NBH;
@@ -994,21 +1046,24 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   };
 
   auto issue = [&](DnMxBuf<WA, RT> &bf, MxItem it) {
-    if (it.u < 0) return;
-    const int q = it.task / NBH, blk = it.task - q * NBH;
-    const int si = it.u / nv, v = it.u - si * nv;
-    const int slot = q + si * kMxGroups;
-    const int e = __builtin_amdgcn_readfirstlane(plan[1 + slot]);
+    const bool live = it.u >= 0 && it.task < ntask;
+    const int task = live ? it.task : 0, u = live ? it.u : 0;
+    const int q = task / NBH, blk = task - q * NBH;
+    const int si = u / nv, v = u - si * nv;
+    const int slot = live ? q + si * kMxGroups : 0;
+    const int e = slot < 64 ? __builtin_amdgcn_readlane(eslot_lo, slot)
+                            : __builtin_amdgcn_readlane(eslot_hi, slot - 64);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
     const uint32_t c0 = (uint32_t)(v * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = blk * 16 * RT + 16 * t + (lane >> 2);
-      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c0, row < H);
+      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c0, live && row < H);
     }
-    mx_load_b(bf.b, rhh, rhl, (uint32_t)(slot * T * m.Ip) * 2u, c0, T, jv);
-    bf.hs = jv ? m.hinv[slot * T + j] : 0.0f;
+    mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, c0, T, live);
+    bf.hs = __builtin_bit_cast(float, buf_load4(rhs, live && bv ? (uint32_t)(slot * T + (j & 7)) * 4u
+                                                                : kOutOfRange));
   };
 
   f4v_t acc[RT];
@@ -1016,16 +1071,14 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   for (int t = 0; t < RT; ++t) acc[t] = f4v_t{0, 0, 0, 0};
   int parity = 0;
 
-  auto consume = [&](const DnMxBuf<WA, RT> &bf, MxItem it) {
-    if (it.u >= 0) {
+  auto consume = [&](const DnMxBuf<WA, RT> &bf, MxItem it) {  // empty items add zeros
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        f4v_t ah = {0, 0, 0, 0}, al = ah;
-        mx_mma(bf.w[t], bf.b, ah, al);
-        acc[t] += (ah + al * (1.0f / kLoScale)) * bf.hs;
-      }
+    for (int t = 0; t < RT; ++t) {
+      f4v_t d = {0, 0, 0, 0};
+      mx_mma(bf.w[t], bf.b, d);
+      acc[t] += d * (bf.hs * part_scale);
     }
-    if (it.u >= 0 && it.u + WA < n_items(it.task)) return;
+    if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_items(it.task))) return;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       red[parity][wave][t][lane] = acc[t];
@@ -1036,9 +1089,13 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
       const int q = it.task / NBH, blk = it.task - q * NBH;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        f4v_t sum = {0, 0, 0, 0};
+        f4v_t sum = {0, 0, 0, 0}, lo = sum;
 #pragma unroll
-        for (int w = 0; w < WA; ++w) sum += red[parity][w][t][lane];
+        for (int w = 0; w < WA; ++w) {
+          sum += red[parity][w][t][lane];
+          lo += red[parity][w][t][lane + 8];
+        }
+        sum += lo;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int orow = blk * 16 * RT + 16 * t + 4 * g + r;
@@ -1051,14 +1108,13 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 
   DnMxBuf<WA, RT> b0, b1;
   MxItem i0 = first(), i1;
-  if (i0.task < ntask) issue(b0, i0);
-  while (i0.task < ntask) {
+  issue(b0, i0);
+  while (i0.task < ntask) {  // in pairs, as in k_gate_up_mx
     i1 = next(i0);
-    if (i1.task < ntask) issue(b1, i1);
+    issue(b1, i1);
     consume(b0, i0);
-    if (i1.task >= ntask) break;
     i0 = next(i1);
-    if (i0.task < ntask) issue(b0, i0);
+    issue(b0, i0);
     consume(b1, i1);
   }
 }
@@ -1258,8 +1314,11 @@ size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
 #ifndef DUCKMOE_MX_DN_WAVES
 #define DUCKMOE_MX_DN_WAVES 4       // waves per down workgroup
 #endif
-#ifndef DUCKMOE_MX_ROW_TILES
-#define DUCKMOE_MX_ROW_TILES 2      // 16-row MFMA tiles per task (they share activation loads)
+#ifndef DUCKMOE_MX_GU_ROW_TILES
+#define DUCKMOE_MX_GU_ROW_TILES 2   // 16-row MFMA tiles per gate/up task (they share B loads)
+#endif
+#ifndef DUCKMOE_MX_DN_ROW_TILES
+#define DUCKMOE_MX_DN_ROW_TILES 2   // 16-row MFMA tiles per down task
 #endif
 #ifndef DUCKMOE_MX_WAVES_PER_CU
 #define DUCKMOE_MX_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
@@ -1270,7 +1329,7 @@ bool use_mx(int T, int n_shards) { return T >= DUCKMOE_MX_MIN_T && n_shards == 1
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct MxLayout {
-  size_t xh, xl, xinv, hh, hl, hinv, part, end;
+  size_t xb, xinv, hb, hinv, part, end;
   int Hp, Ip;
 };
 
@@ -1280,11 +1339,9 @@ MxLayout mx_layout(const duckmoe_layer *L, int T, bool single, size_t base) {
   m.Ip = (L->inter + kMxUnit - 1) / kMxUnit * kMxUnit;
   const size_t slots = hbuf_slots(L, T, single);
   size_t off = align256(base);
-  m.xh = off;   off = align256(off + (size_t)T * m.Hp * 2);
-  m.xl = off;   off = align256(off + (size_t)T * m.Hp * 2);
+  m.xb = off;   off = align256(off + (size_t)2 * T * m.Hp * 2);
   m.xinv = off; off = align256(off + (size_t)T * 4);
-  m.hh = off;   off = align256(off + slots * T * m.Ip * 2);
-  m.hl = off;   off = align256(off + slots * T * m.Ip * 2);
+  m.hb = off;   off = align256(off + slots * 2 * T * m.Ip * 2);
   m.hinv = off; off = align256(off + slots * T * 4);
   m.part = off; off = align256(off + (size_t)kMxGroups * T * L->hidden * 4);
   m.end = off;
@@ -1371,7 +1428,7 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
-  constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_ROW_TILES;
+  constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_GU_ROW_TILES;
   hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   int grid = 0;
@@ -1384,7 +1441,7 @@ hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st
 }
 
 hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
-  constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_ROW_TILES;
+  constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_DN_ROW_TILES;
   int grid = 0;
   hipError_t err = persistent_grid(k_down_mx<WA, RT>, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    (a.H + 16 * RT - 1) / (16 * RT) * kMxGroups, grid);
@@ -1439,11 +1496,9 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
     const MxLayout l = mx_layout(L, T, single, kHdrBytes + hbuf_bytes(L, T, single));
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     MxArgs m;
-    m.xh = reinterpret_cast<_Float16 *>(b + l.xh);
-    m.xl = reinterpret_cast<_Float16 *>(b + l.xl);
+    m.xb = reinterpret_cast<_Float16 *>(b + l.xb);
     m.xinv = reinterpret_cast<float *>(b + l.xinv);
-    m.hh = reinterpret_cast<_Float16 *>(b + l.hh);
-    m.hl = reinterpret_cast<_Float16 *>(b + l.hl);
+    m.hb = reinterpret_cast<_Float16 *>(b + l.hb);
     m.hinv = reinterpret_cast<float *>(b + l.hinv);
     m.part = reinterpret_cast<float *>(b + l.part);
     m.Hp = l.Hp;
