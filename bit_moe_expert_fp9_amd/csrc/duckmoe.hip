@@ -1637,7 +1637,7 @@ int duckmoe_lane_init(duckmoe_lane *lane) {
   if (hipEventCreateWithFlags(&lane->ready, hipEventDisableTiming) != hipSuccess)
     return DUCKMOE_EHIP;
   if (hipEventCreateWithFlags(&lane->done, hipEventDisableTiming) != hipSuccess) {
-    hipEventDestroy(lane->ready);
+    (void)hipEventDestroy(lane->ready);
     lane->ready = nullptr;
     return DUCKMOE_EHIP;
   }
