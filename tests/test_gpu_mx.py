@@ -1,0 +1,137 @@
+"""GPU parity of the matrix-core decode path (3 <= T <= 8 tokens) on the cases
+the random draws of test_gpu_parity.py do not reach: invalid and repeated ids,
+zero routing weights, every token naming the same experts (few slots), every
+id distinct (65 slots at T = 8, top-8: the largest plan, whose last slot the
+down kernel finds in its second word of slot experts), the stage split and
+repeated calls.
+
+Bars as everywhere: f32 outputs within relative L2 <= 1e-5 and max-abs <=
+1e-4 * max|ref| of the float64 oracle; the status word exact; repeated calls
+bit-identical.  The layer has ragged units in both contractions (1040 =
+8 * 128 + 16 hidden, 336 = 2 * 128 + 80 intermediate) and 72 routed experts so
+that 64 distinct ids fit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import OracleExperts, check_close, say
+from lib_util import ensure_built
+
+import bit_moe_expert_fp9_amd as dm
+from bit_moe_expert_fp9_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0
+WL, H, I, E, K = 104, 1040, 336, 72, 8
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU (deselect with -m 'not gpu')")
+    ensure_built()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def layer(torch_dev):
+    say("build matrix-core test layer", WL, H, I, E, K)
+    return dm.Layer(H, I, E, K).fill_synthetic(SEED, WL, 0), OracleExperts(SEED, WL, 0, H, I)
+
+
+def to_dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def call(torch, lay, x, ids, w, ws=None):
+    if ws is None:
+        ws = lay.workspace(x.shape[0])
+    out = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids.astype(np.int32)),
+                       to_dev(torch, w.astype(np.float32)), ws=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), dm.status(ws)
+
+
+def reference(ox, x, ids, w):
+    ox.prefetch([int(i) for i in np.unique(ids) if 0 <= i < E] + [E])
+    return oracle.moe_layer(ox, x, ids, w, E)
+
+
+@pytest.mark.parametrize("T", [3, 8])
+def test_bad_repeated_ids_and_zero_weights(torch_dev, layer, T):
+    torch = torch_dev
+    lay, ox = layer
+    x = synth.activations(SEED, WL, 0, 10 + T, T, H)
+    ids, w = synth.routing(SEED, WL, 0, 10 + T, T, E, K)
+    w = w.astype(np.float32)
+    ids[0, 5] = ids[0, 1]              # a repeat: the two weights add
+    ids[1, 2], ids[2, 7] = -1, E + 3   # out of range: skipped
+    w[T - 1] = 0.0                     # a token with zero weights: shared expert only
+    say("matrix-core path T =", T, "bad, repeated ids, zero weights")
+    got, st = call(torch, lay, x, ids, w)
+    assert st == dm.duckmoe.STATUS_BAD_ID | dm.duckmoe.STATUS_DUP_ID
+    # for the oracle a skipped id is a zero-weight repeat of the token's first id
+    ref_ids, ref_w = ids.copy(), w.astype(np.float64)
+    for t, i in ((1, 2), (2, 7)):
+        ref_ids[t, i] = ids[t, 0]
+        ref_w[t, i] = 0.0
+    ref = reference(ox, x, ref_ids, ref_w)
+    for t in range(T):
+        check_close(got[t], ref[t], "T=%d token %d" % (T, t))
+
+
+def test_every_token_same_experts(torch_dev, layer):
+    torch = torch_dev
+    lay, ox = layer
+    T = 8
+    x = synth.activations(SEED, WL, 0, 30, T, H)
+    _, w = synth.routing(SEED, WL, 0, 30, T, E, K)
+    ids = np.tile(np.array([3, 70, 11, 0, 45, 9, 64, 27], dtype=np.int32), (T, 1))
+    say("matrix-core path, 9 slots for 8 tokens")
+    got, st = call(torch, lay, x, ids, w)
+    assert st == 0
+    check_close(got, reference(ox, x, ids, w), "same experts")
+    assert dm.moe_plan(to_dev(torch, ids), E) == [E, 3, 70, 11, 0, 45, 9, 64, 27]
+
+
+def test_sixty_four_distinct_ids(torch_dev, layer):
+    torch = torch_dev
+    lay, ox = layer
+    T = 8
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(E)[:T * K].reshape(T, K).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    x = synth.activations(SEED, WL, 0, 31, T, H)
+    say("matrix-core path, 65 slots")
+    got, st = call(torch, lay, x, ids, w)
+    assert st == 0
+    plan = dm.moe_plan(to_dev(torch, ids), E)
+    assert len(plan) == 65 and plan[0] == E and plan[1:] == list(ids.ravel())
+    ref = reference(ox, x, ids, w)
+    for t in range(T):
+        check_close(got[t], ref[t], "65 slots token %d" % t)
+
+
+def test_stage_split_and_repeat_calls(torch_dev, layer):
+    torch = torch_dev
+    lay, ox = layer
+    T = 5
+    x = synth.activations(SEED, WL, 0, 32, T, H)
+    ids, w = synth.routing(SEED, WL, 0, 32, T, E, K)
+    xd, idd, wd = to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w.astype(np.float32))
+    say("matrix-core path, stage split and repeat calls")
+    ws = lay.workspace(T)
+    first = dm.moe_layer(lay, xd, idd, wd, ws=ws).cpu().numpy()
+    for _ in range(10):
+        np.testing.assert_array_equal(first, dm.moe_layer(lay, xd, idd, wd, ws=ws).cpu().numpy())
+    ws2 = lay.workspace(T)
+    dm.moe_gate_up(lay, xd, idd, wd, ws2)
+    split = dm.moe_down(lay, xd, idd, wd, ws2).cpu().numpy()
+    np.testing.assert_array_equal(split, first)
+    # down again on the same workspace: the same bits
+    np.testing.assert_array_equal(dm.moe_down(lay, xd, idd, wd, ws2).cpu().numpy(), first)
+    check_close(first, reference(ox, x, ids, w), "T=5")
