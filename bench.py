@@ -93,7 +93,9 @@ def log(*a):
 
 
 def time_layer(torch, dm, layer, T, steps, warmup, draws):
-    """Times `steps` layer calls (after `warmup`) with events around both launches."""
+    """Times `steps` layer calls (after `warmup`): once back to back between two
+    events (the throughput), once with an event before each call (the per-call
+    percentiles)."""
     from bit_moe_expert_fp9_amd import synth
     n = steps + warmup
     xs, ids, ws_, uniq = [], [], [], []
@@ -116,17 +118,28 @@ def time_layer(torch, dm, layer, T, steps, warmup, draws):
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
     torch.cuda.synchronize()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # The timed region: `steps` calls back to back between two events.
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    a.record(stream)
+    for k in range(steps):
+        s = warmup + k
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = a.elapsed_time(b)
+    # The per-call distribution: the same calls again with an event before each
+    # (an event between two calls adds its own gap, so this pass is not the
+    # throughput figure).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for k in range(steps):
         s = warmup + k
         ev[k].record(stream)
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
     ev[steps].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = ev[0].elapsed_time(ev[steps])
     t_call = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
     u = np.array(uniq[warmup:], dtype=np.float64)
     eb = layer.expert_bytes()
@@ -556,6 +569,7 @@ def main():
             "layer_hbm_gbps": gbps,
             "layer_hbm_frac": gbps / HBM_PEAK_GBPS,
             "us_per_layer_p10_p50_p90": [r1["p10_us"], r1["p50_us"], r1["p90_us"]],
+            "us_per_layer_with_events_mean": r1["call_us"],
             "bsz2_tokens_per_s": r2["tokens_per_s"] if r2 else None,
             "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
             "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
