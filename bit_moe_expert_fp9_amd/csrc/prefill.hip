@@ -53,17 +53,30 @@
 namespace duckmoe {
 namespace {
 
-constexpr int kPfTile = 64;                     // entries (tokens) per tile
-constexpr int kPfCols = kPfTile / 16;           // MFMA column tiles per tile
+// Tiles hold 64 entries (tokens), or 96 when the routed lists average more
+// than 48 entries (see pf_tile); the workspace is sized for 64.
+constexpr int kPfTileMin = 64;
+constexpr int kPfTileMax = 96;
 constexpr int kPfWaves = 8;                     // waves per GEMM workgroup
+template <int TILE>
+constexpr int pf_cols() { return TILE / 16; }   // MFMA column tiles per tile
+template <int TILE>
+constexpr int pf_q() { return TILE / 32; }      // token rows a thread stages per unit
+// Launch shapes per tile size: 16-row tiles per wave (RT) and resident
+// workgroups per CU the registers must allow.  At 96 entries the double-buffered
+// activation tile (105 KB of LDS) leaves room for one workgroup per CU, and
+// gate/up takes 32 rows per wave.
 #ifndef DUCKMOE_PF_GU_RT
-#define DUCKMOE_PF_GU_RT 1          // gate/up: 16-row tiles per wave and matrix
+#define DUCKMOE_PF_GU_RT 1          // gate/up, 64-entry tiles
 #endif
 #ifndef DUCKMOE_PF_GU_WG_PER_CU
-#define DUCKMOE_PF_GU_WG_PER_CU 2   // gate/up: resident workgroups per CU the registers must allow
+#define DUCKMOE_PF_GU_WG_PER_CU 2
+#endif
+#ifndef DUCKMOE_PF_GU_RT96
+#define DUCKMOE_PF_GU_RT96 2        // gate/up, 96-entry tiles (one workgroup per CU)
 #endif
 #ifndef DUCKMOE_PF_DN_RT
-#define DUCKMOE_PF_DN_RT 2          // down: 16-row tiles per wave
+#define DUCKMOE_PF_DN_RT 2          // down, both tile sizes (one workgroup per CU)
 #endif
 #ifndef DUCKMOE_PF_DN_WG_PER_CU
 #define DUCKMOE_PF_DN_WG_PER_CU 1
@@ -77,11 +90,12 @@ template <int RT>
 constexpr int pf_rows() { return kPfWaves * RT * 16; }
 template <int RT>
 constexpr int pf_wpu() { return kMxUnit / (RT * 16); }
-static_assert(kPfWaves * 64 * 4 == 2 * kPfTile * (2 * kMxUnit) / 16,
-              "one workgroup stages a unit's hi/lo tile as 4 x 16 bytes per thread");
+static_assert(kPfWaves * 64 == 512 && kMxUnit == 128,
+              "staging: 16 threads per token row of 256 bytes, 32 rows per pass");
 
 struct PfArgs {
   int H, I, E, K, T, Hp, Ip, A;  // A = entry capacity, T * (K + 1)
+  int tile;              // entries per tile (kPfTileMin or kPfTileMax)
   const uint8_t *gu_body, *gu_sign, *dn_body, *dn_sign;
   const float *x;        // [T][H]
   const int32_t *ids;    // [T][K] (K = 0: no routed ids)
@@ -158,18 +172,18 @@ __global__ __launch_bounds__(256) void k_pf_count(const PfArgs a) {
 }
 
 // One workgroup of 1024: counts -> first entries (exclusive scan over lists),
-// the tile table (lists cut into tiles of kPfTile entries) and its size.
+// the tile table (lists cut into tiles of a.tile entries) and its size.
 __global__ __launch_bounds__(1024) void k_pf_scan(const PfArgs a) {
   __shared__ int cnt[kPfMaxRouted + 1];
   __shared__ int se[1024], st[1024];
-  const int n = a.E + 1, tid = threadIdx.x;
+  const int n = a.E + 1, tid = threadIdx.x, tile = a.tile;
   for (int p = tid; p < n; p += 1024) cnt[p] = a.off[p + 1];
   __syncthreads();
   const int per = (n + 1023) / 1024, p0 = min(n, tid * per), p1 = min(n, p0 + per);
   int ce = 0, ct = 0;
   for (int p = p0; p < p1; ++p) {
     ce += cnt[p];
-    ct += (cnt[p] + kPfTile - 1) / kPfTile;
+    ct += (cnt[p] + tile - 1) / tile;
   }
   se[tid] = ce;
   st[tid] = ct;
@@ -185,10 +199,10 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const PfArgs a) {
   for (int p = p0; p < p1; ++p) {
     a.off[p] = eb;
     if (a.tiles) {
-      for (int k = 0; k * kPfTile < cnt[p]; ++k)
-        a.tiles[tb + k] = make_int4(p, eb + k * kPfTile, min(kPfTile, cnt[p] - k * kPfTile), 0);
+      for (int k = 0; k * tile < cnt[p]; ++k)
+        a.tiles[tb + k] = make_int4(p, eb + k * tile, min(tile, cnt[p] - k * tile), 0);
     }
-    tb += (cnt[p] + kPfTile - 1) / kPfTile;
+    tb += (cnt[p] + tile - 1) / tile;
     eb += cnt[p];
   }
   if (tid == 1023) {
@@ -293,39 +307,43 @@ __device__ __forceinline__ int pf_vid() {
   return (b % 8) * (G / 8) + b / 8;
 }
 
-// B staging: a unit's tile is [2 parts][64 tokens][256 bytes]; thread tid moves
-// the 16-byte pieces (part h, token tid / 16 + 32 q, bytes 16 (tid % 16) ..)
-// for h, q in {0, 1}: global -> registers, then registers -> LDS.
+// B staging: a unit's tile is [2 parts][TILE tokens][256 bytes]; thread tid
+// moves the 16-byte pieces (part h, token tid / 16 + 32 q, bytes 16 (tid % 16) ..)
+// for h in {0, 1}, q < Q = TILE / 32: global -> registers, then registers -> LDS.
+template <int Q>
 struct PfStage {
-  uint4 v[2][2];
+  uint4 v[2][Q];
 };
 
-__device__ __forceinline__ void pf_stage_load(PfStage &s, __amdgpu_buffer_rsrc_t rh,
-                                              __amdgpu_buffer_rsrc_t rl, const uint32_t src[2],
+template <int Q>
+__device__ __forceinline__ void pf_stage_load(PfStage<Q> &s, __amdgpu_buffer_rsrc_t rh,
+                                              __amdgpu_buffer_rsrc_t rl, const uint32_t src[Q],
                                               uint32_t ubytes) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const uint32_t o = src[q] == kOutOfRange ? kOutOfRange : src[q] + ubytes;
     s.v[0][q] = buf_load16(rh, o);
     s.v[1][q] = buf_load16(rl, o);
   }
 }
 
-__device__ __forceinline__ void pf_stage_store(const PfStage &s, uint8_t *buf) {
+template <int TILE>
+__device__ __forceinline__ void pf_stage_store(const PfStage<pf_q<TILE>()> &s, uint8_t *buf) {
   const int tok = threadIdx.x >> 4, seg = threadIdx.x & 15;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      *reinterpret_cast<uint4 *>(buf + h * (kPfTile * kPfPitch) + (tok + 32 * q) * kPfPitch +
+    for (int q = 0; q < pf_q<TILE>(); ++q)
+      *reinterpret_cast<uint4 *>(buf + h * (TILE * kPfPitch) + (tok + 32 * q) * kPfPitch +
                                  seg * 16) = s.v[h][q];
 }
 
 // MFMA B operand of lane (token j, group g) for column tile ct and step s.
+template <int TILE>
 __device__ __forceinline__ half8_t pf_b(const uint8_t *buf, int part, int ct, int s) {
   const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int seg = 2 * g + (s & 1) + 8 * (s >> 1);
-  return *reinterpret_cast<const half8_t *>(buf + part * (kPfTile * kPfPitch) +
+  return *reinterpret_cast<const half8_t *>(buf + part * (TILE * kPfPitch) +
                                             (16 * ct + j) * kPfPitch + seg * 16);
 }
 
@@ -339,9 +357,9 @@ __device__ __forceinline__ half8_t pf_a(const h2_t d[8], int ss) {
 // acc[r][m][ct] += A(r, m) * B(ct) over one 128-column unit.  M matrices of
 // RT row tiles each; wm holds the unit's weight tiles in MFMA order; only the
 // first nct column tiles are live.
-template <int RT, int M>
+template <int RT, int M, int TILE>
 __device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t *buf, int nct,
-                                        f4v_t (&acc)[RT][M][kPfCols]) {
+                                        f4v_t (&acc)[RT][M][pf_cols<TILE>()]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     h2_t d[RT][M][8];
@@ -354,9 +372,9 @@ __device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t
     for (int ss = 0; ss < 2; ++ss) {
       const int s = 2 * hf + ss;
 #pragma unroll
-      for (int ct = 0; ct < kPfCols; ++ct) {
+      for (int ct = 0; ct < pf_cols<TILE>(); ++ct) {
         if (ct < nct) {
-          const half8_t bh = pf_b(buf, 0, ct, s), bl = pf_b(buf, 1, ct, s);
+          const half8_t bh = pf_b<TILE>(buf, 0, ct, s), bl = pf_b<TILE>(buf, 1, ct, s);
 #pragma unroll
           for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -374,18 +392,19 @@ __device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t
 // One task of a grouped GEMM: a tile (list, first entry, entries) times a
 // block of kPfRows output rows.  task >= ntask is "no task": no entries, every
 // load out of range.  Scalar fields are wave-uniform.
+template <int Q>
 struct PfTask {
   int task, blk;
   int e0, n, nct;
   const uint8_t *body, *sign;  // the expert's planes of this matrix
-  uint32_t src[2];             // staging sources of this thread, unit 0 (bytes)
+  uint32_t src[Q];             // staging sources of this thread, unit 0 (bytes)
   uint32_t hsrc;               // down: this thread's h' scale source, unit 0 (bytes)
 };
 
-template <bool GU>
-__device__ __forceinline__ PfTask pf_task(const PfArgs &a, int task, int NB, int ntask,
-                                          __amdgpu_buffer_rsrc_t rtok) {
-  PfTask t;
+template <bool GU, int TILE>
+__device__ __forceinline__ PfTask<pf_q<TILE>()> pf_task(const PfArgs &a, int task, int NB,
+                                                        int ntask, __amdgpu_buffer_rsrc_t rtok) {
+  PfTask<pf_q<TILE>()> t;
   t.task = task;
   const bool ok = task < ntask;
   const int tile = ok ? task / NB : 0;
@@ -401,7 +420,7 @@ __device__ __forceinline__ PfTask pf_task(const PfArgs &a, int task, int NB, int
   t.sign = GU ? a.gu_sign + ex * 2 * (mat / 8) : a.dn_sign + ex * (mat / 8);
   const uint32_t seg = threadIdx.x & 15;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < pf_q<TILE>(); ++q) {
     const int tt = (threadIdx.x >> 4) + 32 * q;
     uint32_t row;
     if (GU)  // the token's x row (gathered)
@@ -427,16 +446,16 @@ __device__ __forceinline__ PfTask pf_task(const PfArgs &a, int task, int NB, int
 // next task after a task's last unit) are in flight; every load in the loop is
 // issued unconditionally (out-of-range offsets read zero) so the compiler's
 // wait counts stay exact and never drain the queue.  One barrier per unit.
-template <bool GU, int RT, int WGCU>
+template <bool GU, int RT, int WGCU, int TILE>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     WGCU * kPfWaves / 4, WGCU * kPfWaves / 4))) void k_pf_gemm(const PfArgs a) {
-  constexpr int NT = kPfCols, M = GU ? 2 : 1;
+  constexpr int NT = pf_cols<TILE>(), M = GU ? 2 : 1, Q = pf_q<TILE>();
   constexpr int kPfRows = pf_rows<RT>(), kPfWPU = pf_wpu<RT>();
   static_assert(!GU || (kPfWPU * RT * 16 == kMxUnit && kPfWaves % kPfWPU == 0),
                 "gate/up waves tile the 128-row units of h'");
-  __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * kPfTile * kPfPitch];
-  __shared__ float red[GU ? kPfWaves : 1][kPfTile];
-  __shared__ float lsc[2][GU ? 1 : kPfTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lb[2][2 * TILE * kPfPitch];
+  __shared__ float red[GU ? kPfWaves : 1][TILE];
+  __shared__ float lsc[2][GU ? 1 : TILE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
@@ -455,18 +474,18 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   int task = pf_vid();
   if (task >= ntask) return;
-  PfTask cur = pf_task<GU>(a, task, NB, ntask, rtok);
-  PfTask nxt = pf_task<GU>(a, task + (int)gridDim.x, NB, ntask, rtok);
+  PfTask<Q> cur = pf_task<GU, TILE>(a, task, NB, ntask, rtok);
+  PfTask<Q> nxt = pf_task<GU, TILE>(a, task + (int)gridDim.x, NB, ntask, rtok);
 
-  auto stage_src = [&](const PfTask &t, int u, uint32_t (&src)[2]) {
+  auto stage_src = [&](const PfTask<Q> &t, int u, uint32_t (&src)[Q]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < Q; ++q)
       src[q] = t.src[q] == kOutOfRange ? kOutOfRange : t.src[q] + (uint32_t)u * (2u * kMxUnit);
   };
-  auto scale_src = [&](const PfTask &t, int u) {
+  auto scale_src = [&](const PfTask<Q> &t, int u) {
     return t.hsrc == kOutOfRange ? kOutOfRange : t.hsrc + (uint32_t)u * 4u;
   };
-  auto load_w = [&](MxTile (&w)[RT][M], const PfTask &t, int u) {
+  auto load_w = [&](MxTile (&w)[RT][M], const PfTask<Q> &t, int u) {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.body, mbytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sign, mbytes / 8u);
 #pragma unroll
@@ -491,26 +510,26 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
   };
   zero();
 
-  PfStage stg;
+  PfStage<Q> stg;
   MxTile raw[RT][M];
   float scv = 0.0f;
   {
-    uint32_t src[2];
+    uint32_t src[Q];
     stage_src(cur, 0, src);
     pf_stage_load(stg, rh, rl, src, 0);
     scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(cur, 0)));
     load_w(raw, cur, 0);
-    pf_stage_store(stg, lb[0]);
-    if (!GU && threadIdx.x < kPfTile) lsc[0][threadIdx.x] = scv;
+    pf_stage_store<TILE>(stg, lb[0]);
+    if (!GU && threadIdx.x < TILE) lsc[0][threadIdx.x] = scv;
     __syncthreads();
   }
   int par = 0;
   for (;;) {
     for (int u = 0; u < nu; ++u) {
       const bool last = u + 1 == nu;
-      const PfTask &nt = last ? nxt : cur;
+      const PfTask<Q> &nt = last ? nxt : cur;
       const int un = last ? 0 : u + 1;
-      uint32_t src[2];
+      uint32_t src[Q];
       stage_src(nt, un, src);
       pf_stage_load(stg, rh, rl, src, 0);
       if (!GU) scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(nt, un)));
@@ -521,14 +540,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
         for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
       load_w(raw, nt, un);
       if (GU) {
-        pf_unit<RT, M>(wm, lb[par], cur.nct, acc);
+        pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, acc);
       } else {
         f4v_t tmp[RT][M][NT];
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
-        pf_unit<RT, M>(wm, lb[par], cur.nct, tmp);
+        pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, tmp);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
           if (ct < cur.nct) {
@@ -538,8 +557,8 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
-      pf_stage_store(stg, lb[par ^ 1]);
-      if (!GU && threadIdx.x < kPfTile) lsc[par ^ 1][threadIdx.x] = scv;
+      pf_stage_store<TILE>(stg, lb[par ^ 1]);
+      if (!GU && threadIdx.x < TILE) lsc[par ^ 1][threadIdx.x] = scv;
       __syncthreads();
       par ^= 1;
     }
@@ -623,7 +642,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     zero();
     if (nxt.task >= ntask) break;
     cur = nxt;
-    nxt = pf_task<GU>(a, cur.task + (int)gridDim.x, NB, ntask, rtok);
+    nxt = pf_task<GU, TILE>(a, cur.task + (int)gridDim.x, NB, ntask, rtok);
   }
 }
 
@@ -651,6 +670,35 @@ __global__ __launch_bounds__(256) void k_pf_combine(const PfArgs a) {
 // ------------------------------------------------------------ host side ----
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Entries per tile.  A list longer than a tile streams its expert's weights
+// once per tile.  When the routed lists average 49 to 72 entries, many would
+// spill just past a 64-entry tile into a second one while nearly all fit in
+// 96, so the tiles take 96 entries.  Otherwise the 64-entry tiles keep two
+// workgroups per CU on gate/up (measured faster at T = 256, 1024 and 4096 over
+// 256 experts, top-8; 96 is faster at 2048).  Without routed ids the one list
+// holds every token.
+int pf_tile(int T, int K, int E) {
+  const long mean = (K > 0 && E > 0) ? (long)T * K / E : T;
+  return (mean > 48 && mean <= 72) ? kPfTileMax : kPfTileMin;
+}
+
+// The two grouped GEMMs for one tile size.
+template <int TILE, int RG, int CG, int RD, int CD>
+hipError_t launch_pf_gemms(const PfArgs &a, int max_tiles, hipStream_t stream) {
+  const int threads = kPfWaves * 64;
+  const auto kgu = k_pf_gemm<true, RG, CG, TILE>;
+  const auto kdn = k_pf_gemm<false, RD, CD, TILE>;
+  int g1 = 0, g2 = 0;
+  const int NBi = (a.I + pf_rows<RG>() - 1) / pf_rows<RG>();
+  const int NBh = (a.H + pf_rows<RD>() - 1) / pf_rows<RD>();
+  hipError_t err = persistent_grid(kgu, threads, CG * kPfWaves, max_tiles * NBi, g1);
+  if (err == hipSuccess) err = persistent_grid(kdn, threads, CD * kPfWaves, max_tiles * NBh, g2);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kgu, dim3(g1), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(kdn, dim3(g2), dim3(threads), 0, stream, a);
+  return hipSuccess;
+}
+
 struct PfLayout {
   size_t off, tiles, tok, wt, tok_entry, xh, xl, xinv, hh, hl, hs, y, end;
   int Hp, Ip, A, K, max_tiles;
@@ -662,7 +710,7 @@ PfLayout pf_layout(const duckmoe_layer *L, int T, bool routed) {
   l.Hp = (L->hidden + kMxUnit - 1) / kMxUnit * kMxUnit;
   l.Ip = (L->inter + kMxUnit - 1) / kMxUnit * kMxUnit;
   l.A = T * (l.K + 1);
-  l.max_tiles = (l.A + kPfTile - 1) / kPfTile + L->n_routed + 1;
+  l.max_tiles = (l.A + kPfTileMin - 1) / kPfTileMin + L->n_routed + 1;
   size_t o = 256;  // status word, tile count
   l.off = o;       o = align256(o + (size_t)(L->n_routed + 2) * 4);
   l.tiles = o;     o = align256(o + (size_t)l.max_tiles * 16);
@@ -738,6 +786,7 @@ int duckmoe_moe_prefill(const duckmoe_layer *L, const float *x, const int32_t *i
   a.Hp = l.Hp;
   a.Ip = l.Ip;
   a.A = l.A;
+  a.tile = pf_tile(T, l.K, L->n_routed);
   a.gu_body = L->gu_body;
   a.gu_sign = L->gu_sign;
   a.dn_body = L->dn_body;
@@ -763,19 +812,13 @@ int duckmoe_moe_prefill(const duckmoe_layer *L, const float *x, const int32_t *i
 
   if (launch_plan(a, stream) != hipSuccess) return DUCKMOE_EHIP;
   hipLaunchKernelGGL(k_pf_xprep, dim3(T), dim3(256), 0, stream, a);
-  const int threads = kPfWaves * 64;
-  constexpr int RG = DUCKMOE_PF_GU_RT, RD = DUCKMOE_PF_DN_RT;
-  constexpr int CG = DUCKMOE_PF_GU_WG_PER_CU, CD = DUCKMOE_PF_DN_WG_PER_CU;
-  const auto kgu = k_pf_gemm<true, RG, CG>;
-  const auto kdn = k_pf_gemm<false, RD, CD>;
-  int g1 = 0, g2 = 0;
-  const int NBi = (a.I + pf_rows<RG>() - 1) / pf_rows<RG>();
-  const int NBh = (a.H + pf_rows<RD>() - 1) / pf_rows<RD>();
-  if (persistent_grid(kgu, threads, CG * kPfWaves, l.max_tiles * NBi, g1) != hipSuccess ||
-      persistent_grid(kdn, threads, CD * kPfWaves, l.max_tiles * NBh, g2) != hipSuccess)
-    return DUCKMOE_EHIP;
-  hipLaunchKernelGGL(kgu, dim3(g1), dim3(threads), 0, stream, a);
-  hipLaunchKernelGGL(kdn, dim3(g2), dim3(threads), 0, stream, a);
+  const hipError_t err =
+      a.tile == kPfTileMax
+          ? launch_pf_gemms<kPfTileMax, DUCKMOE_PF_GU_RT96, 1, DUCKMOE_PF_DN_RT,
+                            DUCKMOE_PF_DN_WG_PER_CU>(a, l.max_tiles, stream)
+          : launch_pf_gemms<kPfTileMin, DUCKMOE_PF_GU_RT, DUCKMOE_PF_GU_WG_PER_CU,
+                            DUCKMOE_PF_DN_RT, DUCKMOE_PF_DN_WG_PER_CU>(a, l.max_tiles, stream);
+  if (err != hipSuccess) return DUCKMOE_EHIP;
   const size_t n4 = (size_t)T * (a.H / 4);
   hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DUCKMOE_OK : DUCKMOE_EHIP;
@@ -798,6 +841,7 @@ int duckmoe_prefill_plan(const int32_t *ids, const float *w, int32_t T, int32_t 
   a.status = status;
   a.n_tiles = nullptr;
   a.tiles = nullptr;
+  a.tile = kPfTileMin;  // no tile table is written; the scan still counts tiles
   a.off = offsets;
   a.tok = tokens;
   a.wt = weights;
