@@ -19,16 +19,17 @@
 //     range is skipped; both are flagged in the status word).  Entries are
 //     numbered list by list; tok_entry[t] names token t's entries (shared
 //     first, then by id position, -1 for a repeat or a bad id).  Lists are cut
-//     into tiles of 64 entries.  Only per-list scans, a block scan and a
-//     ballot: no atomics, the same lists every call.
+//     into tiles of 64 entries, or 96 (pf_tile).  Only per-list scans, a block
+//     scan and a ballot: no atomics, the same lists every call.
 //   k_pf_xprep: x rows -> fp16 hi/lo pairs (below).
-//   k_pf_gate_up: a workgroup of 8 waves takes tasks (tile, block of 256
-//     intermediate rows): each wave owns 32 gate rows and the matching 32 up
-//     rows, the tile's activations of each 128-column unit are staged once in
-//     LDS for all 8 waves, and the epilogue writes h' = w * silu(gate) * up as
-//     scaled fp16 hi/lo pairs per (entry, 128-row unit).
-//   k_pf_down: the same grouped GEMM over (tile, block of 256 output rows) with
-//     the down weights, writing y[entry][H] in f32.
+//   k_pf_gemm (gate/up): a workgroup of 8 waves takes tasks (tile, block of
+//     8 * 16 * RT intermediate rows): each wave owns 16 * RT gate rows and the
+//     matching up rows, the tile's activations of each 128-column unit are
+//     staged once in LDS for all 8 waves, and the epilogue writes
+//     h' = w * silu(gate) * up as scaled fp16 hi/lo pairs per (entry, 128-row
+//     unit).
+//   k_pf_gemm (down): the same grouped GEMM over (tile, block of output rows)
+//     with the down weights, writing y[entry][H] in f32.
 //   k_pf_combine: out_t = the entries of tok_entry[t] added in slot order.
 // Every output element is a fixed-order sum: bit-identical run to run.
 //
@@ -53,8 +54,8 @@
 namespace duckmoe {
 namespace {
 
-// Tiles hold 64 entries (tokens), or 96 when the routed lists average more
-// than 48 entries (see pf_tile); the workspace is sized for 64.
+// Tiles hold 64 entries (tokens), or 96 when the routed lists average 49 to 72
+// entries (see pf_tile); the workspace is sized for 64.
 constexpr int kPfTileMin = 64;
 constexpr int kPfTileMax = 96;
 constexpr int kPfWaves = 8;                     // waves per GEMM workgroup
