@@ -218,6 +218,24 @@ def test_prefill_matches_decode_path(torch_dev, layers):
             check_close(a[t], b[t], "prefill vs decode T=%d token %d" % (T, t))
 
 
+@pytest.mark.parametrize("T", [144, 147, 216, 219])
+def test_prefill_tile_size_boundaries(torch_dev, layers, T):
+    """The call cuts its lists into 96-entry tiles when the routed lists average
+    49 to 72 entries, else 64: with 24 experts and top-8 that is T = 147 .. 218.
+    Both sides of both boundaries against the oracle (every 7th token and the
+    last)."""
+    torch = torch_dev
+    lay, ox = layers[180]
+    say("prefill tile-size boundary T =", T)
+    x, ids, w, got, ws = run_prefill(torch, lay, ox, 180, 500 + T, T)
+    assert dm.status(ws) == 0
+    toks = sorted(set(range(0, T, 7)) | {T - 1})
+    ox.prefetch(list(np.unique(ids[toks])) + [lay.n_routed])
+    ref = oracle.moe_layer(ox, x[toks], ids[toks], w[toks], lay.n_routed)
+    for i, t in enumerate(toks):
+        check_close(got[t], ref[i], "tile boundary T=%d token %d" % (T, t))
+
+
 def test_prefill_largest_batch(torch_dev):
     """T = 32768 (the call's limit) on a small layer: sampled tokens against the
     oracle (tokens at tile edges, the first and the last)."""
