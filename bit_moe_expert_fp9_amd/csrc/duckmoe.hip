@@ -832,7 +832,7 @@ __device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t r, ui
 
 // acc += A * B over the unit's 4 steps (columns j: hi of token j, 8 + j: its lo)
 __device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &acc) {
-  const MxTile w = mx_to_mfma(wl);
+  const MxFrag w = mx_to_mfma(wl);
   h2_t d[16];
   fp9_decode16(w.b0, w.s0, d);
   fp9_decode16(w.b1, w.s1, d + 8);
@@ -870,7 +870,7 @@ struct GuMxBuf {
   MxAct b;
 };
 
-template <int WA, int RT>
+template <int WA, int RT, bool SA>
 __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT * 2][64];
   const int lane = threadIdx.x & 63;
@@ -908,8 +908,8 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = r0 + 16 * t + (lane >> 2);
-      mx_load_w(bf.g[t], rb, rs, (uint32_t)row, H, c0, live && row < I);
-      mx_load_w(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, live && row < I);
+      mx_load_w<SA>(bf.g[t], rb, rs, (uint32_t)row, H, c0, live && row < I);
+      mx_load_w<SA>(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, live && row < I);
     }
     mx_load_b(bf.b, rx, 0u, c0, T, live);
   };
@@ -1005,7 +1005,7 @@ struct DnMxBuf {
   float hs;
 };
 
-template <int WA, int RT>
+template <int WA, int RT, bool SA>
 __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT][64];
   const int32_t *plan = reinterpret_cast<const int32_t *>(
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = blk * 16 * RT + 16 * t + (lane >> 2);
-      mx_load_w(bf.w[t], rb, rs, (uint32_t)row, I, c0, live && row < H);
+      mx_load_w<SA>(bf.w[t], rb, rs, (uint32_t)row, I, c0, live && row < H);
     }
     mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, c0, T, live);
     bf.hs = __builtin_bit_cast(float, buf_load4(rhs, live && bv ? (uint32_t)(slot * T + (j & 7)) * 4u
@@ -1427,26 +1427,45 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
   }
 }
 
-hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+template <bool SA>
+hipError_t launch_mx_gate_up_sa(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_GU_ROW_TILES;
-  hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
+  const auto kern = k_gate_up_mx<WA, RT, SA>;
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   int grid = 0;
-  hipError_t err = persistent_grid(k_gate_up_mx<WA, RT>, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+  hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    max_slots * ((a.I + 16 * RT - 1) / (16 * RT)), grid);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((k_gate_up_mx<WA, RT>), dim3(grid), dim3(WA * 64), 0, st, a, m);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), 0, st, a, m);
+  return hipSuccess;
+}
+
+hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
+  const hipError_t err = mx_sign_aligned(a.H) ? launch_mx_gate_up_sa<true>(a, m, st)
+                                              : launch_mx_gate_up_sa<false>(a, m, st);
+  if (err != hipSuccess) return err;
+  const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   hipLaunchKernelGGL(k_mx_hprep, dim3(max_slots * a.T), dim3(256), 0, st, a, m);
   return hipGetLastError();
 }
 
-hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+template <bool SA>
+hipError_t launch_mx_down_sa(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_DN_ROW_TILES;
+  const auto kern = k_down_mx<WA, RT, SA>;
   int grid = 0;
-  hipError_t err = persistent_grid(k_down_mx<WA, RT>, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+  hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    (a.H + 16 * RT - 1) / (16 * RT) * kMxGroups, grid);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((k_down_mx<WA, RT>), dim3(grid), dim3(WA * 64), 0, st, a, m);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), 0, st, a, m);
+  return hipSuccess;
+}
+
+hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  const hipError_t err = mx_sign_aligned(a.I) ? launch_mx_down_sa<true>(a, m, st)
+                                              : launch_mx_down_sa<false>(a, m, st);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_mx_reduce, dim3((a.T * a.H + 255) / 256), dim3(256), 0, st, a, m);
   return hipGetLastError();
 }

@@ -15,6 +15,14 @@
 // holds columns 16g .. 16g + 15 (MFMA steps 0 and 1: 8 columns each) and
 // 64 + 16g .. 64 + 16g + 15 (steps 2 and 3), so in step s the group's 8
 // columns are 16g + 8 (s & 1) + 64 (s >> 1) .. + 7, and B must follow them.
+//
+// The unit's 16 sign bytes of row i are loaded as one dword per lane (lane
+// 4i + q: bytes 4q .. 4q + 3), 16 bytes per row in one request, instead of two
+// 2-byte loads per lane (8 bytes per row and request): the address unit
+// handles each request of a wave's load separately, and the matrix-core
+// kernels are bound by it.  Lane i + 16g then takes its two 16-bit words,
+// bytes 2g, 2g + 1 and 8 + 2g, 9 + 2g, from lanes 4i + g / 2 and
+// 4i + 2 + g / 2 with two ds_bpermute.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,39 +47,65 @@ __device__ __forceinline__ int mx_scale_exp(float m) {
   return max(-126, min(126, 14 - e));
 }
 
-struct MxTile {     // one unit of one 16-row tile for one lane
+struct MxTile {     // one unit of one 16-row tile for one lane, as loaded
   uint4 b0, b1;     // 2 x 16 body bytes (see the layout note)
+  uint32_t s;       // sign bytes 4q .. 4q + 3 of the unit's 16 in this row
+};
+
+struct MxFrag {     // the same unit moved to MFMA lane order
+  uint4 b0, b1;     // columns 16g .. 16g + 15 and 64 + 16g .. 64 + 16g + 15 of row i
   uint16_t s0, s1;  // their sign bits (16 + 16)
 };
 
 // Load lane 4i + q's share: row `row` (= the tile's row i), columns
-// c0 + 16q .. and c0 + 64 + 16q .. (16 each) of a [rows][K] matrix.  Rows with
-// rv false and columns at or past K read as zero.
+// c0 + 16q .. and c0 + 64 + 16q .. (16 each) of a [rows][K] matrix, and sign
+// bytes c0 / 8 + 4q .. + 3 of the row (columns c0 + 32q .. c0 + 32q + 31).
+// Rows with rv false and columns at or past K read as zero (a sign word that
+// starts below K may end past it; its extra bits belong to columns whose body
+// reads as zero, so they only choose the sign of a zero).  SA: the sign rows
+// are whole dwords (K % 32 == 0), so the four bytes are one dword load;
+// otherwise they are two 2-byte loads (dword loads must be dword-aligned).
+template <bool SA>
 __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
                                           __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
                                           uint32_t c0, bool rv) {
-  const uint32_t c = c0 + 16 * (threadIdx.x & 3);
-  const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
+  const uint32_t q = threadIdx.x & 3;
+  const uint32_t c = c0 + 16 * q;
+  const bool v0 = rv && c < K, v1 = rv && c + 64 < K, vs = rv && c0 + 32 * q < K;
   w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
   w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
-  w.s0 = buf_load2h(rs, v0 ? row * (K / 8) + c / 8 : kOutOfRange);
-  w.s1 = buf_load2h(rs, v1 ? row * (K / 8) + c / 8 + 8 : kOutOfRange);
+  const uint32_t so = row * (K / 8) + c0 / 8 + 4 * q;
+  if (SA) {
+    w.s = buf_load4(rs, vs ? so : kOutOfRange);
+  } else {
+    const bool vs1 = rv && c0 + 32 * q + 16 < K;
+    w.s = (uint32_t)buf_load2h(rs, vs ? so : kOutOfRange) |
+          ((uint32_t)buf_load2h(rs, vs1 ? so + 2 : kOutOfRange) << 16);
+  }
 }
 
-// Move lane 4i + g's tile words to lane i + 16g.  The empty volatile asm
-// consumes the loaded sign words here: without it the compiler may hoist the
-// arithmetic that merges them above an earlier barrier, which makes that
-// barrier wait for loads meant to stay in flight across it.
-__device__ __forceinline__ MxTile mx_to_mfma(const MxTile &w) {
+// Whether the sign rows of a matrix with K columns are whole dwords.
+__host__ __device__ constexpr bool mx_sign_aligned(int K) { return K % 32 == 0; }
+
+// Move lane 4i + g's body words to lane i + 16g and gather its sign words
+// (see the layout note).  The empty volatile asm consumes the loaded sign word
+// here: without it the compiler may move work on it above an earlier barrier,
+// which makes that barrier wait for loads meant to stay in flight across it.
+__device__ __forceinline__ MxFrag mx_to_mfma(const MxTile &w) {
   const int l = threadIdx.x & 63;
-  const int src = 4 * ((4 * (l & 15) + (l >> 4)) & 63);  // byte address of lane 4(l % 16) + l / 16
+  const int i = l & 15, g = l >> 4;
+  const int src = 4 * (4 * i + g);  // byte address of lane 4i + g
   auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
-  uint16_t s0 = w.s0, s1 = w.s1;
-  asm volatile("" : "+v"(s0), "+v"(s1));
-  MxTile o;
+  uint32_t s = w.s;
+  asm volatile("" : "+v"(s));
+  MxFrag o;
   o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
   o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
-  const uint32_t sg = mv((uint32_t)s0 | ((uint32_t)s1 << 16));
+  // bytes 2g, 2g + 1 sit in dword g / 2 of the row, bytes 8 + 2g, 9 + 2g in
+  // dword 2 + g / 2; half g % 2 of each
+  const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + (g >> 1)), (int)s);
+  const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + 2 + (g >> 1)), (int)s);
+  const uint32_t sg = __builtin_amdgcn_perm(y, x, (g & 1) ? 0x07060302u : 0x05040100u);
   o.s0 = (uint16_t)(sg & 0xFFFFu);
   o.s1 = (uint16_t)(sg >> 16);
   return o;

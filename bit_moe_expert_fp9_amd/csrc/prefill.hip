@@ -359,7 +359,7 @@ __device__ __forceinline__ half8_t pf_a(const h2_t d[8], int ss) {
 // RT row tiles each; wm holds the unit's weight tiles in MFMA order; only the
 // first nct column tiles are live.
 template <int RT, int M, int TILE>
-__device__ __forceinline__ void pf_unit(const MxTile (&wm)[RT][M], const uint8_t *buf, int nct,
+__device__ __forceinline__ void pf_unit(const MxFrag (&wm)[RT][M], const uint8_t *buf, int nct,
                                         f4v_t (&acc)[RT][M][pf_cols<TILE>()]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -447,7 +447,7 @@ __device__ __forceinline__ PfTask<pf_q<TILE>()> pf_task(const PfArgs &a, int tas
 // next task after a task's last unit) are in flight; every load in the loop is
 // issued unconditionally (out-of-range offsets read zero) so the compiler's
 // wait counts stay exact and never drain the queue.  One barrier per unit.
-template <bool GU, int RT, int WGCU, int TILE>
+template <bool GU, int RT, int WGCU, int TILE, bool SA>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     WGCU * kPfWaves / 4, WGCU * kPfWaves / 4))) void k_pf_gemm(const PfArgs a) {
   constexpr int NT = pf_cols<TILE>(), M = GU ? 2 : 1, Q = pf_q<TILE>();
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
       const bool rv = row < rows && t.n > 0;
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        mx_load_w(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
+        mx_load_w<SA>(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
                   (uint32_t)(u * kMxUnit), rv);
     }
   };
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
       stage_src(nt, un, src);
       pf_stage_load(stg, rh, rl, src, 0);
       if (!GU) scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(nt, un)));
-      MxTile wm[RT][M];
+      MxFrag wm[RT][M];
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -683,21 +683,28 @@ int pf_tile(int T, int K, int E) {
   return (mean > 48 && mean <= 72) ? kPfTileMax : kPfTileMin;
 }
 
-// The two grouped GEMMs for one tile size.
+// One grouped GEMM (gate/up or down) for one tile size and sign-row alignment.
+template <bool GU, int RT, int WGCU, int TILE, bool SA>
+hipError_t launch_pf_gemm(const PfArgs &a, int max_tiles, hipStream_t stream) {
+  const int threads = kPfWaves * 64;
+  const auto kern = k_pf_gemm<GU, RT, WGCU, TILE, SA>;
+  int grid = 0;
+  const int NB = ((GU ? a.I : a.H) + pf_rows<RT>() - 1) / pf_rows<RT>();
+  const hipError_t err = persistent_grid(kern, threads, WGCU * kPfWaves, max_tiles * NB, grid);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, stream, a);
+  return hipSuccess;
+}
+
+// The two grouped GEMMs for one tile size (gate/up contracts over H, down
+// over I; each picks its sign-load width by its own row length).
 template <int TILE, int RG, int CG, int RD, int CD>
 hipError_t launch_pf_gemms(const PfArgs &a, int max_tiles, hipStream_t stream) {
-  const int threads = kPfWaves * 64;
-  const auto kgu = k_pf_gemm<true, RG, CG, TILE>;
-  const auto kdn = k_pf_gemm<false, RD, CD, TILE>;
-  int g1 = 0, g2 = 0;
-  const int NBi = (a.I + pf_rows<RG>() - 1) / pf_rows<RG>();
-  const int NBh = (a.H + pf_rows<RD>() - 1) / pf_rows<RD>();
-  hipError_t err = persistent_grid(kgu, threads, CG * kPfWaves, max_tiles * NBi, g1);
-  if (err == hipSuccess) err = persistent_grid(kdn, threads, CD * kPfWaves, max_tiles * NBh, g2);
+  hipError_t err = mx_sign_aligned(a.H) ? launch_pf_gemm<true, RG, CG, TILE, true>(a, max_tiles, stream)
+                                        : launch_pf_gemm<true, RG, CG, TILE, false>(a, max_tiles, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kgu, dim3(g1), dim3(threads), 0, stream, a);
-  hipLaunchKernelGGL(kdn, dim3(g2), dim3(threads), 0, stream, a);
-  return hipSuccess;
+  return mx_sign_aligned(a.I) ? launch_pf_gemm<false, RD, CD, TILE, true>(a, max_tiles, stream)
+                              : launch_pf_gemm<false, RD, CD, TILE, false>(a, max_tiles, stream);
 }
 
 struct PfLayout {
