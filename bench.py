@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=16,
                    help="tokens (bsz 1 steps) the oracle times for the CPU baseline")
     p.add_argument("--bsz2", type=int, default=1, help="also time bsz 2 (0 to skip)")
+    p.add_argument("--more-bsz", type=str, default="4,8",
+                   help="comma-separated further batch sizes (3..8, the matrix-core path) timed "
+                        "on the same layer ('' to skip); results go under config.layer_bsz")
     p.add_argument("--stack", action="store_true",
                    help="also time the 16-layer stack (about 204 GB of fp9 weights drawn on the "
                         "device) at bsz 1, 2, 4 and 8; results go under 'stack'")
@@ -543,6 +546,16 @@ def main():
         r2 = time_layer(torch, dm, layer, 2, args.steps, args.warmup, draws)
         log("bsz2:", json.dumps(r2))
 
+    more = {}
+    for T in [int(v) for v in args.more_bsz.split(",") if v.strip()]:
+        r = time_layer(torch, dm, layer, T, min(args.steps, 300), min(args.warmup, 20), draws)
+        more[str(T)] = {"us_per_layer": r["ms_per_step"] * 1e3,
+                        "tokens_per_s": r["tokens_per_s"],
+                        "mean_experts": r["mean_experts"],
+                        "hbm_gbps": r["bytes_step"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                        "hbm_frac": r["bytes_step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log("bsz%d:" % T, json.dumps(more[str(T)]))
+
     st1 = time_stages(torch, dm, layer, 1, args.steps, args.warmup, draws)
     log("bsz1 stages:", json.dumps(st1))
 
@@ -582,6 +595,7 @@ def main():
             "bsz2_tokens_per_s": r2["tokens_per_s"] if r2 else None,
             "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
             "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
+            "layer_bsz": more or None,
             "stages_us": {"k_gate_up": st1["gate_up_us"], "k_down": st1["down_us"]},
             "read_ceiling": {"what": "plain streaming read of the same byte count, one launch, "
                                      "fresh window, HIP events (duckmoe_read_probe)",
