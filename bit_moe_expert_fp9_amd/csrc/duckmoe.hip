@@ -831,8 +831,7 @@ __device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t r, ui
 }
 
 // acc += A * B over the unit's 4 steps (columns j: hi of token j, 8 + j: its lo)
-__device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &acc) {
-  const MxFrag w = mx_to_mfma(wl);
+__device__ __forceinline__ void mx_mma_frag(const MxFrag &w, const MxAct &b, f4v_t &acc) {
   h2_t d[16];
   fp9_decode16(w.b0, w.s0, d);
   fp9_decode16(w.b1, w.s1, d + 8);
@@ -846,47 +845,56 @@ __device__ __forceinline__ void mx_mma(const MxTile &wl, const MxAct &b, f4v_t &
 }
 
 // A wave's work in the two matrix-core kernels is one flat stream of items:
-// for each task of its workgroup (in order), the units u = wave, wave + WA, ...
-// of the task, or one empty item (u = -1) when the wave has no unit in it, so
-// that every wave closes every task exactly once (the close has a barrier).
-// The loads of the next item, possibly in the next task, are issued before the
-// current one is computed.  Every item issues the same loads, an empty item or
-// one past the last task with out-of-range offsets (they read zeros and touch
-// no memory): with a branch around them the compiler could not know how many
-// loads are in flight behind the current item's, and its waits would drain the
-// next item's loads as well.
+// for each task of its workgroup (in order), the unit pairs p = wave,
+// wave + WA, ... of the task (units 2p and 2p + 1, the second one empty past
+// the task's last unit), or one empty pair (p = -1) when the wave has no pair
+// in it, so that every wave closes every task exactly once (the close has a
+// barrier).  A pair is two items, one per unit; the sign words of both units
+// come with the first item's loads (mx_load_signs) and are kept in one of two
+// alternating register sets.  The loads of the next item, possibly in the
+// next task, are issued before the current one is computed.  Every item
+// issues the same loads, an empty item or one past the last task with
+// out-of-range offsets (they read zeros and touch no memory): with a branch
+// around them the compiler could not know how many loads are in flight behind
+// the current item's, and its waits would drain the next item's loads as well.
 struct MxItem {
   int task;
-  int u;  // unit index, -1 for the empty item
+  int u;  // pair index, -1 for the empty pair
 };
 
 // Gate/up: a workgroup of WA waves takes whole tasks (slot, block of 16 * RT
-// rows) and splits the task's units (128 columns of H) over its waves; the
+// rows) and splits the task's unit pairs (256 columns of H) over its waves; the
 // waves' partial accumulators meet in LDS, wave 0 sums them in a fixed order and
 // writes h' = w * silu(gate) * up for the block's rows and every token.
-template <int WA, int RT>
+template <int RT>
 struct GuMxBuf {
-  MxTile g[RT], u[RT];
+  MxBody g[RT], u[RT];
   MxAct b;
 };
 
-template <int WA, int RT, bool SA>
+template <int RT>
+struct GuMxSigns {
+  MxSigns g[RT], u[RT];
+};
+
+template <int WA, int RT, int SM>
 __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT * 2][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H, I = a.I, T = a.T;
   const int nu = m.Hp / kMxUnit;
+  const int np = (nu + 1) / 2;
   const int NB = (I + 16 * RT - 1) / (16 * RT);  // row blocks per slot (last may be partial)
   const PlanIn pin = plan_load(a);
   const WavePlan plan = wave_plan(a, pin);
   if (blockIdx.x == 0 && wave == 0) plan_store(plan, a);
   const int ntask = plan.n_slots * NB;
   // tasks blockIdx.x, blockIdx.x + gridDim.x, ...
-  auto first = [&]() { return MxItem{(int)blockIdx.x, wave < nu ? wave : -1}; };
+  auto first = [&]() { return MxItem{(int)blockIdx.x, wave < np ? wave : -1}; };
   auto next = [&](MxItem it) {
-    if (it.u >= 0 && it.u + WA < nu) return MxItem{it.task, it.u + WA};
-    return MxItem{it.task + (int)gridDim.x, wave < nu ? wave : -1};
+    if (it.u >= 0 && it.u + WA < np) return MxItem{it.task, it.u + WA};
+    return MxItem{it.task + (int)gridDim.x, wave < np ? wave : -1};
   };
   const int j = lane & 15, g = lane >> 4;
   const uint32_t mat = (uint32_t)I * (uint32_t)H;
@@ -897,21 +905,28 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   float xs = __builtin_bit_cast(float, buf_load4(make_rsrc(m.xinv, (uint32_t)T * 4u),
                                                  jv ? (uint32_t)j * 4u : kOutOfRange));
 
-  auto issue = [&](GuMxBuf<WA, RT> &bf, MxItem it) {
-    const bool live = it.u >= 0 && it.task < ntask;
-    const int task = live ? it.task : 0, u = live ? it.u : 0;
+  // unit 2p + half of the item's pair; the first half also loads both units' signs
+  auto issue = [&](GuMxBuf<RT> &bf, GuMxSigns<RT> &sg, MxItem it, int half) {
+    const bool live = it.u >= 0 && it.task < ntask && 2 * it.u + half < nu;
+    const int task = live ? it.task : 0, u = live ? 2 * it.u : 0;
     const int slot = task / NB, r0 = (task - slot * NB) * 16 * RT;
     const int e = plan_expert(plan, slot);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.gu_body + (size_t)e * 2 * mat, 2 * mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gu_sign + (size_t)e * 2 * (mat / 8), 2 * (mat / 8));
     const uint32_t c0 = (uint32_t)(u * kMxUnit);
+    const uint32_t ch = c0 + (uint32_t)(half * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = r0 + 16 * t + (lane >> 2);
-      mx_load_w<SA>(bf.g[t], rb, rs, (uint32_t)row, H, c0, live && row < I);
-      mx_load_w<SA>(bf.u[t], rb, rs, (uint32_t)(I + row), H, c0, live && row < I);
+      const bool rv = live && row < I;
+      mx_load_body(bf.g[t], rb, (uint32_t)row, H, ch, rv);
+      mx_load_body(bf.u[t], rb, (uint32_t)(I + row), H, ch, rv);
+      if (half == 0) {
+        mx_load_signs<SM>(sg.g[t], rs, (uint32_t)row, H, c0, rv);
+        mx_load_signs<SM>(sg.u[t], rs, (uint32_t)(I + row), H, c0, rv);
+      }
     }
-    mx_load_b(bf.b, rx, 0u, c0, T, live);
+    mx_load_b(bf.b, rx, 0u, ch, T, live);
   };
 
   f4v_t acc[RT][2];  // gate, up
@@ -926,14 +941,21 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
 
   // An empty item's tiles are zeros and add nothing; computing them anyway
   // consumes every load, so no register of the item is still being written
-  // when the next issue reuses it.
-  auto consume = [&](const GuMxBuf<WA, RT> &bf, MxItem it) {
+  // when the next issue reuses it.  The second half closes the task.
+  auto consume0 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      mx_mma(bf.g[t], bf.b, acc[t][0]);
-      mx_mma(bf.u[t], bf.b, acc[t][1]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
-    if (it.task >= ntask || (it.u >= 0 && it.u + WA < nu)) return;
+  };
+  auto consume1 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg, MxItem it) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
+    }
+    if (it.task >= ntask || (it.u >= 0 && it.u + WA < np)) return;
     // close the task: partials to LDS, wave 0 reduces and writes h' (lane j < 8
     // adds the hi sums of its own column and the lo sums of column 8 + j)
 #pragma unroll
@@ -974,38 +996,49 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
     parity ^= 1;
   };
 
-  GuMxBuf<WA, RT> b0, b1;
-  MxItem i0 = first(), i1;
-  issue(b0, i0);
+  GuMxBuf<RT> b0, b1;
+  GuMxSigns<RT> s0, s1;
+  MxItem p0 = first(), p1;
+  issue(b0, s0, p0, 0);
   asm volatile("" : "+v"(xs));  // xs arrives here, the first item stays in flight
-  // Items go in pairs; the second of the last pair may lie past the last task
-  // (zeros, no close).  No exit between the two halves: a path that leaves with
-  // one buffer's loads unconsumed would make the compiler's waits at the loop
-  // head assume those loads may still be writing their registers.
-  while (i0.task < ntask) {
-    i1 = next(i0);
-    issue(b1, i1);
-    consume(b0, i0);
-    i0 = next(i1);
-    issue(b0, i0);
-    consume(b1, i1);
+  // Two pairs per trip; the second may lie past the last task (zeros, no
+  // close).  No exit inside a trip: a path that leaves with one buffer's loads
+  // unconsumed would make the compiler's waits at the loop head assume those
+  // loads may still be writing their registers.
+  while (p0.task < ntask) {
+    issue(b1, s0, p0, 1);
+    consume0(b0, s0);
+    p1 = next(p0);
+    issue(b0, s1, p1, 0);
+    consume1(b1, s0, p0);
+    issue(b1, s1, p1, 1);
+    consume0(b0, s1);
+    p0 = next(p1);
+    issue(b0, s0, p0, 0);
+    consume1(b1, s1, p1);
   }
 }
 
 // Down: a workgroup takes tasks (block of 16 * RT rows of H, slot group q) and
-// splits the (slot, unit of I) items of the group's slots over its waves; each
-// item's accumulator is unscaled into the wave's running sum (column j by the
-// token's scale, column 8 + j by that scale times 2^-11); the waves' sums meet
-// in LDS and wave 0 writes the group's partial for the block's rows, adding
-// columns j and 8 + j.  The groups' partials are added by k_mx_reduce in a fixed order.
-template <int WA, int RT>
+// splits the (slot, unit pair of I) items of the group's slots over its waves;
+// each unit's accumulator is unscaled into the wave's running sum (column j by
+// the token's scale, column 8 + j by that scale times 2^-11); the waves' sums
+// meet in LDS and wave 0 writes the group's partial for the block's rows,
+// adding columns j and 8 + j.  The groups' partials are added by k_mx_reduce in
+// a fixed order.
+template <int RT>
 struct DnMxBuf {
-  MxTile w[RT];
+  MxBody w[RT];
   MxAct b;
-  float hs;
 };
 
-template <int WA, int RT, bool SA>
+template <int RT>
+struct DnMxSigns {
+  MxSigns w[RT];
+  float hs;  // the (slot, token) row's unscale factor, for both units
+};
+
+template <int WA, int RT, int SM>
 __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT][64];
   const int32_t *plan = reinterpret_cast<const int32_t *>(
@@ -1019,6 +1052,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   const int eslot_lo = plan[1 + lane];
   const int eslot_hi = plan[1 + min(64 + lane, kMaxIds)];
   const int nv = m.Ip / kMxUnit;
+  const int npv = (nv + 1) / 2;  // unit pairs per slot
   const int NBH = (H + 16 * RT - 1) / (16 * RT);
   const int ntask = NBH * kMxGroups;
   const int j = lane & 15, g = lane >> 4;
@@ -1029,41 +1063,45 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   const int max_slots = a.ids != nullptr ? T * a.top_k + 1 : 1;
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(m.hb, (uint32_t)(max_slots * 2 * T * m.Ip) * 2u);
   const __amdgpu_buffer_rsrc_t rhs = make_rsrc(m.hinv, (uint32_t)(max_slots * T) * 4u);
-  // items of the task's group: (slot q + s * G, unit v) for s < ns_q, v < nv
-  auto n_items = [&](int task) {
+  // pairs of the task's group: (slot q + s * G, unit pair vp) for s < ns_q, vp < npv
+  auto n_pairs = [&](int task) {
     const int q = task / NBH;
-    return (S > q ? (S - q + kMxGroups - 1) / kMxGroups : 0) * nv;
+    return (S > q ? (S - q + kMxGroups - 1) / kMxGroups : 0) * npv;
   };
-  // the stream of items as in k_gate_up_mx, with a per-task item count
+  // the stream of pairs as in k_gate_up_mx, with a per-task pair count
   auto first = [&]() {
     const int t = blockIdx.x;
-    return MxItem{t, (t < ntask && wave < n_items(t)) ? wave : -1};
+    return MxItem{t, (t < ntask && wave < n_pairs(t)) ? wave : -1};
   };
   auto next = [&](MxItem it) {
-    if (it.u >= 0 && it.u + WA < n_items(it.task)) return MxItem{it.task, it.u + WA};
+    if (it.u >= 0 && it.u + WA < n_pairs(it.task)) return MxItem{it.task, it.u + WA};
     const int t = it.task + (int)gridDim.x;
-    return MxItem{t, (t < ntask && wave < n_items(t)) ? wave : -1};
+    return MxItem{t, (t < ntask && wave < n_pairs(t)) ? wave : -1};
   };
 
-  auto issue = [&](DnMxBuf<WA, RT> &bf, MxItem it) {
-    const bool live = it.u >= 0 && it.task < ntask;
-    const int task = live ? it.task : 0, u = live ? it.u : 0;
+  auto issue = [&](DnMxBuf<RT> &bf, DnMxSigns<RT> &sg, MxItem it, int half) {
+    const bool pl = it.u >= 0 && it.task < ntask;
+    const int task = pl ? it.task : 0, p = pl ? it.u : 0;
     const int q = task / NBH, blk = task - q * NBH;
-    const int si = u / nv, v = u - si * nv;
-    const int slot = live ? q + si * kMxGroups : 0;
+    const int si = p / npv, vp = p - si * npv;
+    const bool live = pl && 2 * vp + half < nv;
+    const int slot = pl ? q + si * kMxGroups : 0;
     const int e = slot < 64 ? __builtin_amdgcn_readlane(eslot_lo, slot)
                             : __builtin_amdgcn_readlane(eslot_hi, slot - 64);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dn_sign + (size_t)e * (mat / 8), mat / 8);
-    const uint32_t c0 = (uint32_t)(v * kMxUnit);
+    const uint32_t c0 = (uint32_t)(2 * vp * kMxUnit);
+    const uint32_t ch = c0 + (uint32_t)(half * kMxUnit);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = blk * 16 * RT + 16 * t + (lane >> 2);
-      mx_load_w<SA>(bf.w[t], rb, rs, (uint32_t)row, I, c0, live && row < H);
+      mx_load_body(bf.w[t], rb, (uint32_t)row, I, ch, live && row < H);
+      if (half == 0) mx_load_signs<SM>(sg.w[t], rs, (uint32_t)row, I, c0, pl && row < H);
     }
-    mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, c0, T, live);
-    bf.hs = __builtin_bit_cast(float, buf_load4(rhs, live && bv ? (uint32_t)(slot * T + (j & 7)) * 4u
-                                                                : kOutOfRange));
+    mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, ch, T, live);
+    if (half == 0)
+      sg.hs = __builtin_bit_cast(float, buf_load4(rhs, pl && bv ? (uint32_t)(slot * T + (j & 7)) * 4u
+                                                               : kOutOfRange));
   };
 
   f4v_t acc[RT];
@@ -1071,14 +1109,22 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   for (int t = 0; t < RT; ++t) acc[t] = f4v_t{0, 0, 0, 0};
   int parity = 0;
 
-  auto consume = [&](const DnMxBuf<WA, RT> &bf, MxItem it) {  // empty items add zeros
+  auto consume0 = [&](const DnMxBuf<RT> &bf, const DnMxSigns<RT> &sg) {  // empty items add zeros
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma(bf.w[t], bf.b, d);
-      acc[t] += d * (bf.hs * part_scale);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.w[t], sg.w[t]), bf.b, d);
+      acc[t] += d * (sg.hs * part_scale);
     }
-    if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_items(it.task))) return;
+  };
+  auto consume1 = [&](const DnMxBuf<RT> &bf, const DnMxSigns<RT> &sg, MxItem it) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      f4v_t d = {0, 0, 0, 0};
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.w[t], sg.w[t]), bf.b, d);
+      acc[t] += d * (sg.hs * part_scale);
+    }
+    if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_pairs(it.task))) return;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       red[parity][wave][t][lane] = acc[t];
@@ -1106,16 +1152,21 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
     parity ^= 1;
   };
 
-  DnMxBuf<WA, RT> b0, b1;
-  MxItem i0 = first(), i1;
-  issue(b0, i0);
-  while (i0.task < ntask) {  // in pairs, as in k_gate_up_mx
-    i1 = next(i0);
-    issue(b1, i1);
-    consume(b0, i0);
-    i0 = next(i1);
-    issue(b0, i0);
-    consume(b1, i1);
+  DnMxBuf<RT> b0, b1;
+  DnMxSigns<RT> s0, s1;
+  MxItem p0 = first(), p1;
+  issue(b0, s0, p0, 0);
+  while (p0.task < ntask) {  // two pairs per trip, as in k_gate_up_mx
+    issue(b1, s0, p0, 1);
+    consume0(b0, s0);
+    p1 = next(p0);
+    issue(b0, s1, p1, 0);
+    consume1(b1, s0, p0);
+    issue(b1, s1, p1, 1);
+    consume0(b0, s1);
+    p0 = next(p1);
+    issue(b0, s0, p0, 0);
+    consume1(b1, s1, p1);
   }
 }
 
@@ -1427,10 +1478,10 @@ hipError_t launch_down(const LayerArgs &a, hipStream_t st) {
   }
 }
 
-template <bool SA>
-hipError_t launch_mx_gate_up_sa(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+template <int SM>
+hipError_t launch_mx_gate_up_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_GU_ROW_TILES;
-  const auto kern = k_gate_up_mx<WA, RT, SA>;
+  const auto kern = k_gate_up_mx<WA, RT, SM>;
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   int grid = 0;
   hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
@@ -1442,18 +1493,20 @@ hipError_t launch_mx_gate_up_sa(const LayerArgs &a, const MxArgs &m, hipStream_t
 
 hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
-  const hipError_t err = mx_sign_aligned(a.H) ? launch_mx_gate_up_sa<true>(a, m, st)
-                                              : launch_mx_gate_up_sa<false>(a, m, st);
+  const int sm = mx_sign_mode(a.H, a.gu_sign);
+  const hipError_t err = sm == 2   ? launch_mx_gate_up_sm<2>(a, m, st)
+                         : sm == 1 ? launch_mx_gate_up_sm<1>(a, m, st)
+                                   : launch_mx_gate_up_sm<0>(a, m, st);
   if (err != hipSuccess) return err;
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
   hipLaunchKernelGGL(k_mx_hprep, dim3(max_slots * a.T), dim3(256), 0, st, a, m);
   return hipGetLastError();
 }
 
-template <bool SA>
-hipError_t launch_mx_down_sa(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+template <int SM>
+hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_DN_ROW_TILES;
-  const auto kern = k_down_mx<WA, RT, SA>;
+  const auto kern = k_down_mx<WA, RT, SM>;
   int grid = 0;
   hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    (a.H + 16 * RT - 1) / (16 * RT) * kMxGroups, grid);
@@ -1463,8 +1516,10 @@ hipError_t launch_mx_down_sa(const LayerArgs &a, const MxArgs &m, hipStream_t st
 }
 
 hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
-  const hipError_t err = mx_sign_aligned(a.I) ? launch_mx_down_sa<true>(a, m, st)
-                                              : launch_mx_down_sa<false>(a, m, st);
+  const int sm = mx_sign_mode(a.I, a.dn_sign);
+  const hipError_t err = sm == 2   ? launch_mx_down_sm<2>(a, m, st)
+                         : sm == 1 ? launch_mx_down_sm<1>(a, m, st)
+                                   : launch_mx_down_sm<0>(a, m, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_mx_reduce, dim3((a.T * a.H + 255) / 256), dim3(256), 0, st, a, m);
   return hipGetLastError();

@@ -120,6 +120,10 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 __device__ __forceinline__ float4 buf_loadf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

@@ -84,8 +84,11 @@ __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
   }
 }
 
-// Whether the sign rows of a matrix with K columns are whole dwords.
-__host__ __device__ constexpr bool mx_sign_aligned(int K) { return K % 32 == 0; }
+// Whether the sign rows of a matrix with K columns, sign plane at `sign`, are
+// whole, dword-aligned dwords.
+__host__ inline bool mx_sign_aligned(int K, const void *sign) {
+  return K % 32 == 0 && reinterpret_cast<uintptr_t>(sign) % 4 == 0;
+}
 
 // Move lane 4i + g's body words to lane i + 16g and gather its sign words
 // (see the layout note).  The empty volatile asm consumes the loaded sign word
@@ -105,6 +108,104 @@ __device__ __forceinline__ MxFrag mx_to_mfma(const MxTile &w) {
   // dword 2 + g / 2; half g % 2 of each
   const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + (g >> 1)), (int)s);
   const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + 2 + (g >> 1)), (int)s);
+  const uint32_t sg = __builtin_amdgcn_perm(y, x, (g & 1) ? 0x07060302u : 0x05040100u);
+  o.s0 = (uint16_t)(sg & 0xFFFFu);
+  o.s1 = (uint16_t)(sg >> 16);
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Unit pairs (the decode kernels).  A wave that takes units 2p and 2p + 1 of
+// the same rows one after the other loads the sign bytes of both with one
+// request per row where the rows allow it: the address unit's cost is per
+// load instruction, so a second dword in the same instruction is nearly free.
+// Sign modes, by the column count K of the matrix:
+//   2: K % 64 == 0: one 8-byte load per lane, lane 4i + q taking bytes
+//      8q .. 8q + 7 of the pair's 32 (units 2p: q = 0, 1; 2p + 1: q = 2, 3);
+//      8-byte aligned, and a lane's 64 columns lie all below K or all past it;
+//   1: K % 32 == 0: one dword per lane and unit, as in mx_load_w;
+//   0: two 2-byte loads per lane and unit.
+// The mode also needs the sign plane's base aligned to the load width (the
+// expert and row offsets then are: K % 16 == 0 for every matrix).
+__host__ inline int mx_sign_mode(int K, const void *sign) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(sign);
+  return (K % 64 == 0 && p % 8 == 0) ? 2 : ((K % 32 == 0 && p % 4 == 0) ? 1 : 0);
+}
+
+struct MxBody {     // one unit of one 16-row tile for one lane, as loaded
+  uint4 b0, b1;
+};
+
+struct MxSigns {    // the lane's sign words of a unit pair (layout by sign mode)
+  uint32_t a, b;
+};
+
+// The body part of mx_load_w.
+__device__ __forceinline__ void mx_load_body(MxBody &w, __amdgpu_buffer_rsrc_t rb, uint32_t row,
+                                             uint32_t K, uint32_t c0, bool rv) {
+  const uint32_t c = c0 + 16 * (threadIdx.x & 3);
+  w.b0 = buf_load16(rb, rv && c < K ? row * K + c : kOutOfRange);
+  w.b1 = buf_load16(rb, rv && c + 64 < K ? row * K + c + 64 : kOutOfRange);
+}
+
+// The sign words of row `row` for the units starting at columns c0 and
+// c0 + 128; columns at or past K (and rows with rv false) read as zero.
+template <int SM>
+__device__ __forceinline__ void mx_load_signs(MxSigns &s, __amdgpu_buffer_rsrc_t rs, uint32_t row,
+                                              uint32_t K, uint32_t c0, bool rv) {
+  const uint32_t q = threadIdx.x & 3;
+  const uint32_t so = row * (K / 8) + c0 / 8;
+  if (SM == 2) {
+    const uint2 v = buf_load8(rs, rv && c0 + 64 * q < K ? so + 8 * q : kOutOfRange);
+    s.a = v.x;
+    s.b = v.y;
+  } else if (SM == 1) {
+    s.a = buf_load4(rs, rv && c0 + 32 * q < K ? so + 4 * q : kOutOfRange);
+    s.b = buf_load4(rs, rv && c0 + 128 + 32 * q < K ? so + 16 + 4 * q : kOutOfRange);
+  } else {
+    auto half = [&](uint32_t col, uint32_t off) {
+      return (uint32_t)buf_load2h(rs, rv && col < K ? off : kOutOfRange);
+    };
+    s.a = half(c0 + 32 * q, so + 4 * q) | (half(c0 + 32 * q + 16, so + 4 * q + 2) << 16);
+    s.b = half(c0 + 128 + 32 * q, so + 16 + 4 * q) |
+          (half(c0 + 128 + 32 * q + 16, so + 18 + 4 * q) << 16);
+  }
+}
+
+// mx_to_mfma for unit HALF (0: 2p, 1: 2p + 1) of a pair.  Lane i + 16g needs
+// dwords g / 2 and 2 + g / 2 of its unit's 16 sign bytes of row i.  In sign
+// mode 2 those sit in the .a (g < 2) or .b (g >= 2) word of lane 4i + 2 HALF
+// (dwords 0, 1) and 4i + 2 HALF + 1 (dwords 2, 3); one quad-local DPP move
+// per word first gathers, in v1, dword 0 / 1 of each unit on its even / odd
+// lane and, in v2, dword 2 / 3, so that each needed dword is one ds_bpermute
+// away.  In the other modes the unit's word is laid out as in mx_load_w.
+template <int SM, int HALF>
+__device__ __forceinline__ MxFrag mx_to_mfma_pair(const MxBody &w, const MxSigns &sp) {
+  const int l = threadIdx.x & 63;
+  const int i = l & 15, g = l >> 4;
+  const int src = 4 * (4 * i + g);
+  auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
+  uint32_t sa = sp.a, sb = sp.b;
+  asm volatile("" : "+v"(sa), "+v"(sb));
+  MxFrag o;
+  o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
+  o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
+  uint32_t x, y;
+  if (SM == 2) {
+    const bool odd = (l & 1) != 0;
+    // quad_perm [0, 0, 2, 2] of .b and [1, 1, 3, 3] of .a
+    const uint32_t bl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sb, 0xA0, 0xF, 0xF, false);
+    const uint32_t ar = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sa, 0xF5, 0xF, 0xF, false);
+    const uint32_t v1 = odd ? bl : sa;
+    const uint32_t v2 = odd ? sb : ar;
+    const int from = 4 * (4 * i + 2 * HALF + (g >> 1));
+    x = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)v1);
+    y = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)v2);
+  } else {
+    const uint32_t s = HALF ? sb : sa;
+    x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + (g >> 1)), (int)s);
+    y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + 2 + (g >> 1)), (int)s);
+  }
   const uint32_t sg = __builtin_amdgcn_perm(y, x, (g & 1) ? 0x07060302u : 0x05040100u);
   o.s0 = (uint16_t)(sg & 0xFFFFu);
   o.s1 = (uint16_t)(sg >> 16);

@@ -700,10 +700,10 @@ hipError_t launch_pf_gemm(const PfArgs &a, int max_tiles, hipStream_t stream) {
 // over I; each picks its sign-load width by its own row length).
 template <int TILE, int RG, int CG, int RD, int CD>
 hipError_t launch_pf_gemms(const PfArgs &a, int max_tiles, hipStream_t stream) {
-  hipError_t err = mx_sign_aligned(a.H) ? launch_pf_gemm<true, RG, CG, TILE, true>(a, max_tiles, stream)
+  hipError_t err = mx_sign_aligned(a.H, a.gu_sign) ? launch_pf_gemm<true, RG, CG, TILE, true>(a, max_tiles, stream)
                                         : launch_pf_gemm<true, RG, CG, TILE, false>(a, max_tiles, stream);
   if (err != hipSuccess) return err;
-  return mx_sign_aligned(a.I) ? launch_pf_gemm<false, RD, CD, TILE, true>(a, max_tiles, stream)
+  return mx_sign_aligned(a.I, a.dn_sign) ? launch_pf_gemm<false, RD, CD, TILE, true>(a, max_tiles, stream)
                               : launch_pf_gemm<false, RD, CD, TILE, false>(a, max_tiles, stream);
 }
 

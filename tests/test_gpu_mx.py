@@ -3,7 +3,8 @@ the random draws of test_gpu_parity.py do not reach: invalid and repeated ids,
 zero routing weights, every token naming the same experts (few slots), every
 id distinct (65 slots at T = 8, top-8: the largest plan, whose last slot the
 down kernel finds in its second word of slot experts), the stage split and
-repeated calls.
+repeated calls, and each of the three ways the weight tiles load their sign
+bytes.
 
 Bars as everywhere: f32 outputs within relative L2 <= 1e-5 and max-abs <=
 1e-4 * max|ref| of the float64 oracle; the status word exact; repeated calls
@@ -114,6 +115,45 @@ def test_sixty_four_distinct_ids(torch_dev, layer):
     ref = reference(ox, x, ids, w)
     for t in range(T):
         check_close(got[t], ref[t], "65 slots token %d" % t)
+
+
+# Sign-load modes of the unit-pair loads, by column count: 1056 and 352 have
+# sign rows of whole dwords but not of 8-byte words (one dword per lane and
+# unit); 1088 and 320 have 8-byte rows (one 8-byte load per lane and pair) and
+# a last unit only half inside the matrix; 1152 and 640 have 8-byte rows and
+# an odd number of whole units, so each row's last pair has an empty second
+# unit.  (The module's 1040 / 336 layer takes two 2-byte loads per unit.)
+MODE_LAYERS = {  # workload: (H, I, n_routed, top_k)
+    105: (1056, 352, 24, 8),
+    106: (1088, 320, 24, 8),
+    107: (1152, 640, 20, 6),
+}
+
+
+@pytest.fixture(scope="module")
+def mode_layers(torch_dev):
+    out = {}
+    for wl, (h, i, e, k) in MODE_LAYERS.items():
+        say("build sign-mode layer", wl, (h, i, e, k))
+        out[wl] = (dm.Layer(h, i, e, k).fill_synthetic(SEED, wl, 0), OracleExperts(SEED, wl, 0, h, i))
+    return out
+
+
+@pytest.mark.parametrize("wl", sorted(MODE_LAYERS))
+@pytest.mark.parametrize("T", [3, 6, 8])
+def test_sign_load_modes(torch_dev, mode_layers, wl, T):
+    torch = torch_dev
+    lay, ox = mode_layers[wl]
+    h, _, e, k = MODE_LAYERS[wl]
+    x = synth.activations(SEED, wl, 0, 40 + T, T, h)
+    ids, w = synth.routing(SEED, wl, 0, 40 + T, T, e, k)
+    say("matrix-core path, layer", wl, "T =", T)
+    got, st = call(torch, lay, x, ids, w)
+    assert st == 0
+    ox.prefetch([int(i) for i in np.unique(ids)] + [e])
+    ref = oracle.moe_layer(ox, x, ids, w, e)
+    for t in range(T):
+        check_close(got[t], ref[t], "layer %d T=%d token %d" % (wl, T, t))
 
 
 def test_stage_split_and_repeat_calls(torch_dev, layer):
