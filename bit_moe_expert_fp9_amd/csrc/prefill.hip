@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/duckmoe.h"
 #include "fp9_device.h"
@@ -447,7 +448,11 @@ __device__ __forceinline__ PfTask<pf_q<TILE>()> pf_task(const PfArgs &a, int tas
 // next task after a task's last unit) are in flight; every load in the loop is
 // issued unconditionally (out-of-range offsets read zero) so the compiler's
 // wait counts stay exact and never drain the queue.  One barrier per unit.
-template <bool GU, int RT, int WGCU, int TILE, bool SA>
+// SM is the sign-load form (mx_sign_mode); in form 2 the units of a task come
+// in pairs (the host picks it only for an even unit count): the odd unit's
+// loads also fetch the sign bytes of the next pair, which the next two units
+// decode.
+template <bool GU, int RT, int WGCU, int TILE, int SM>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     WGCU * kPfWaves / 4, WGCU * kPfWaves / 4))) void k_pf_gemm(const PfArgs a) {
   constexpr int NT = pf_cols<TILE>(), M = GU ? 2 : 1, Q = pf_q<TILE>();
@@ -495,8 +500,31 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
       const bool rv = row < rows && t.n > 0;
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        mx_load_w<SA>(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
-                  (uint32_t)(u * kMxUnit), rv);
+        mx_load_w<SM == 1>(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
+                           (uint32_t)(u * kMxUnit), rv);
+    }
+  };
+  // form 2: the body of unit u, and (signs) the sign words of units u, u + 1
+  auto load_body = [&](MxBody (&w)[RT][M], const PfTask<Q> &t, int u) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.body, mbytes);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = t.blk * kPfRows + wave * RT * 16 + 16 * r + (lane >> 2);
+      const bool rv = row < rows && t.n > 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        mx_load_body(w[r][m], rb, (uint32_t)(m * I + row), (uint32_t)Kd, (uint32_t)(u * kMxUnit), rv);
+    }
+  };
+  auto load_signs = [&](MxSigns (&w)[RT][M], const PfTask<Q> &t, int u) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sign, mbytes / 8u);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = t.blk * kPfRows + wave * RT * 16 + 16 * r + (lane >> 2);
+      const bool rv = row < rows && t.n > 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        mx_load_signs<2>(w[r][m], rs, (uint32_t)(m * I + row), (uint32_t)Kd, (uint32_t)(u * kMxUnit), rv);
     }
   };
 
@@ -512,56 +540,84 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
   zero();
 
   PfStage<Q> stg;
-  MxTile raw[RT][M];
+  MxTile raw[RT][M];     // forms 0 and 1
+  MxBody rawb[RT][M];    // form 2: the unit's body ...
+  MxSigns sgn[RT][M];    // ... and its pair's sign words
   float scv = 0.0f;
   {
     uint32_t src[Q];
     stage_src(cur, 0, src);
     pf_stage_load(stg, rh, rl, src, 0);
     scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(cur, 0)));
-    load_w(raw, cur, 0);
+    if constexpr (SM == 2) {
+      load_body(rawb, cur, 0);
+      load_signs(sgn, cur, 0);
+    } else {
+      load_w(raw, cur, 0);
+    }
     pf_stage_store<TILE>(stg, lb[0]);
     if (!GU && threadIdx.x < TILE) lsc[0][threadIdx.x] = scv;
     __syncthreads();
   }
   int par = 0;
-  for (;;) {
-    for (int u = 0; u < nu; ++u) {
-      const bool last = u + 1 == nu;
-      const PfTask<Q> &nt = last ? nxt : cur;
-      const int un = last ? 0 : u + 1;
-      uint32_t src[Q];
-      stage_src(nt, un, src);
-      pf_stage_load(stg, rh, rl, src, 0);
-      if (!GU) scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(nt, un)));
-      MxFrag wm[RT][M];
+  // One unit: decode its weights (loaded one unit ahead), issue the next
+  // unit's loads, compute against the staged activations, stage the next ones.
+  // HALF is the unit's place in its pair (form 2 only).
+  auto step = [&](int u, auto half) {
+    constexpr int HALF = decltype(half)::value;
+    const bool last = u + 1 == nu;
+    const PfTask<Q> &nt = last ? nxt : cur;
+    const int un = last ? 0 : u + 1;
+    uint32_t src[Q];
+    stage_src(nt, un, src);
+    pf_stage_load(stg, rh, rl, src, 0);
+    if (!GU) scv = __builtin_bit_cast(float, buf_load4(rhs, scale_src(nt, un)));
+    MxFrag wm[RT][M];
+    if constexpr (SM == 2) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma_pair<2, HALF>(rawb[r][m], sgn[r][m]);
+      load_body(rawb, nt, un);
+      if (HALF == 1) load_signs(sgn, nt, un);  // un starts the next pair
+    } else {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
       load_w(raw, nt, un);
-      if (GU) {
-        pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, acc);
-      } else {
-        f4v_t tmp[RT][M][NT];
+    }
+    if (GU) {
+      pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, acc);
+    } else {
+      f4v_t tmp[RT][M][NT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-          for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
-        pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, tmp);
+        for (int ct = 0; ct < NT; ++ct) tmp[r][0][ct] = f4v_t{0, 0, 0, 0};
+      pf_unit<RT, M, TILE>(wm, lb[par], cur.nct, tmp);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          if (ct < cur.nct) {
-            const float sc = lsc[par][16 * ct + j];
+      for (int ct = 0; ct < NT; ++ct) {
+        if (ct < cur.nct) {
+          const float sc = lsc[par][16 * ct + j];
 #pragma unroll
-            for (int r = 0; r < RT; ++r) acc[r][0][ct] += tmp[r][0][ct] * sc;
-          }
+          for (int r = 0; r < RT; ++r) acc[r][0][ct] += tmp[r][0][ct] * sc;
         }
       }
-      pf_stage_store<TILE>(stg, lb[par ^ 1]);
-      if (!GU && threadIdx.x < TILE) lsc[par ^ 1][threadIdx.x] = scv;
-      __syncthreads();
-      par ^= 1;
+    }
+    pf_stage_store<TILE>(stg, lb[par ^ 1]);
+    if (!GU && threadIdx.x < TILE) lsc[par ^ 1][threadIdx.x] = scv;
+    __syncthreads();
+    par ^= 1;
+  };
+  for (;;) {
+    if constexpr (SM == 2) {
+      for (int u = 0; u < nu; u += 2) {
+        step(u, std::integral_constant<int, 0>());
+        step(u + 1, std::integral_constant<int, 1>());
+      }
+    } else {
+      for (int u = 0; u < nu; ++u) step(u, std::integral_constant<int, 0>());
     }
 
     const int r0 = cur.blk * kPfRows + wave * RT * 16;  // the wave's first row
@@ -684,10 +740,10 @@ int pf_tile(int T, int K, int E) {
 }
 
 // One grouped GEMM (gate/up or down) for one tile size and sign-row alignment.
-template <bool GU, int RT, int WGCU, int TILE, bool SA>
+template <bool GU, int RT, int WGCU, int TILE, int SM>
 hipError_t launch_pf_gemm(const PfArgs &a, int max_tiles, hipStream_t stream) {
   const int threads = kPfWaves * 64;
-  const auto kern = k_pf_gemm<GU, RT, WGCU, TILE, SA>;
+  const auto kern = k_pf_gemm<GU, RT, WGCU, TILE, SM>;
   int grid = 0;
   const int NB = ((GU ? a.I : a.H) + pf_rows<RT>() - 1) / pf_rows<RT>();
   const hipError_t err = persistent_grid(kern, threads, WGCU * kPfWaves, max_tiles * NB, grid);
@@ -696,15 +752,43 @@ hipError_t launch_pf_gemm(const PfArgs &a, int max_tiles, hipStream_t stream) {
   return hipSuccess;
 }
 
+// The sign-load form of one GEMM: that of its weight matrix (K columns, K_p
+// padded to whole units), pairs only for an even unit count.
+int pf_sign_mode(int K, int Kp, const void *sign) {
+  const int sm = mx_sign_mode(K, sign);
+  return (sm == 2 && (Kp / kMxUnit) % 2 != 0) ? 1 : sm;
+}
+
+// Pairs for a kernel configuration (measured): the gate/up kernel with 96-entry
+// tiles has no registers to spare for the second unit's sign words (it spills
+// and runs slower), so it keeps one sign load per unit.
+#ifndef DUCKMOE_PF_PAIR_GU96
+#define DUCKMOE_PF_PAIR_GU96 0
+#endif
+#ifndef DUCKMOE_PF_PAIR_DN96
+#define DUCKMOE_PF_PAIR_DN96 1
+#endif
+template <bool GU, int TILE>
+constexpr bool pf_pairs() {
+  return TILE != kPfTileMax || (GU ? DUCKMOE_PF_PAIR_GU96 : DUCKMOE_PF_PAIR_DN96);
+}
+
+template <bool GU, int RT, int WGCU, int TILE>
+hipError_t launch_pf_gemm_sm(const PfArgs &a, int max_tiles, hipStream_t stream) {
+  int sm = GU ? pf_sign_mode(a.H, a.Hp, a.gu_sign) : pf_sign_mode(a.I, a.Ip, a.dn_sign);
+  if (!pf_pairs<GU, TILE>() && sm == 2) sm = 1;
+  return sm == 2   ? launch_pf_gemm<GU, RT, WGCU, TILE, pf_pairs<GU, TILE>() ? 2 : 1>(a, max_tiles, stream)
+         : sm == 1 ? launch_pf_gemm<GU, RT, WGCU, TILE, 1>(a, max_tiles, stream)
+                   : launch_pf_gemm<GU, RT, WGCU, TILE, 0>(a, max_tiles, stream);
+}
+
 // The two grouped GEMMs for one tile size (gate/up contracts over H, down
-// over I; each picks its sign-load width by its own row length).
+// over I; each picks its sign-load form by its own matrix).
 template <int TILE, int RG, int CG, int RD, int CD>
 hipError_t launch_pf_gemms(const PfArgs &a, int max_tiles, hipStream_t stream) {
-  hipError_t err = mx_sign_aligned(a.H, a.gu_sign) ? launch_pf_gemm<true, RG, CG, TILE, true>(a, max_tiles, stream)
-                                        : launch_pf_gemm<true, RG, CG, TILE, false>(a, max_tiles, stream);
+  const hipError_t err = launch_pf_gemm_sm<true, RG, CG, TILE>(a, max_tiles, stream);
   if (err != hipSuccess) return err;
-  return mx_sign_aligned(a.I, a.dn_sign) ? launch_pf_gemm<false, RD, CD, TILE, true>(a, max_tiles, stream)
-                              : launch_pf_gemm<false, RD, CD, TILE, false>(a, max_tiles, stream);
+  return launch_pf_gemm_sm<false, RD, CD, TILE>(a, max_tiles, stream);
 }
 
 struct PfLayout {
