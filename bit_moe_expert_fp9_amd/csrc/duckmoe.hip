@@ -15,17 +15,17 @@
 //    TP）", section "形态一：Mac-to-Mac 张量并行（RDMA）" (f32 partials).
 //
 // How it maps to CDNA (gfx950): the layer is a weight-streaming GEMV (about 2
-// flops per weight byte at bsz 1), so it is HBM-bound and uses the vector ALUs,
-// not MFMA.  Two launches per layer:
-//   k_gate_up: one workgroup per (expert slot, block of intermediate rows).
-//     Each wave owns P (gate row, up row) pairs and walks the hidden dimension
-//     in 1024-weight chunks: every lane loads 16 body bytes (one 128-bit load)
+// flops per weight byte at bsz 1), so it is HBM-bound and, at bsz 1-2, uses the
+// vector ALUs, not MFMA.  Two launches per layer:
+//   k_gate_up: persistent; each wave takes (expert slot, P intermediate rows)
+//     tasks in a strided sequence and walks the hidden dimension in
+//     1024-weight chunks: every lane loads 16 body bytes (one 128-bit load)
 //     and 2 sign bytes per row, decodes them in registers and FMAs them against
 //     the activation slice it reads from LDS (x is staged there once per
-//     workgroup).  At the end the wave sums its lanes with DPP, applies SwiGLU
-//     and the routing weight, and stores h' = w * silu(g) * v (f32) in the
-//     workspace.
-//   k_down: one workgroup per block of R output rows.  Its waves split the
+//     workgroup).  At a task's end the wave sums its lanes with DPP, applies
+//     SwiGLU and the routing weight, and stores h' = w * silu(g) * v (f32) in
+//     the workspace.  Block 0 also publishes the plan (the distinct experts).
+//   k_down: persistent over blocks of R output rows.  A block's waves split the
 //     (expert slot, 1024-wide chunk of the intermediate dimension) items, each
 //     wave streaming the R down rows of its items and FMAing them against h'.
 //     Because the routing weight is already folded into h', the weighted
@@ -33,6 +33,11 @@
 //     whose width matches the shard slice, and the waves' partial sums are
 //     added in LDS in a fixed order: every output element is written once, no
 //     atomics, bit-reproducible run to run.
+// From 3 tokens on (no shard partials) the two contractions run on the matrix
+// cores instead (k_mx_xprep, k_gate_up_mx, k_mx_hprep, k_down_mx, k_mx_reduce):
+// the fp9 weights decode exactly to fp16 A tiles, the activations are split
+// into scaled fp16 hi and lo parts that share one B operand, and the sums are
+// recombined and unscaled in f32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

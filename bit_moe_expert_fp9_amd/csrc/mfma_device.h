@@ -64,7 +64,8 @@ struct MxFrag {     // the same unit moved to MFMA lane order
 // starts below K may end past it; its extra bits belong to columns whose body
 // reads as zero, so they only choose the sign of a zero).  SA: the sign rows
 // are whole dwords (K % 32 == 0), so the four bytes are one dword load;
-// otherwise they are two 2-byte loads (dword loads must be dword-aligned).
+// otherwise they are two 2-byte loads (dword loads must be dword-aligned; see
+// mx_sign_mode for the choice).
 template <bool SA>
 __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
                                           __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
@@ -82,12 +83,6 @@ __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
     w.s = (uint32_t)buf_load2h(rs, vs ? so : kOutOfRange) |
           ((uint32_t)buf_load2h(rs, vs1 ? so + 2 : kOutOfRange) << 16);
   }
-}
-
-// Whether the sign rows of a matrix with K columns, sign plane at `sign`, are
-// whole, dword-aligned dwords.
-__host__ inline bool mx_sign_aligned(int K, const void *sign) {
-  return K % 32 == 0 && reinterpret_cast<uintptr_t>(sign) % 4 == 0;
 }
 
 // Move lane 4i + g's body words to lane i + 16g and gather its sign words
