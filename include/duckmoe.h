@@ -89,9 +89,10 @@ extern "C" {
  * expert is index 0, run with duckmoe_expert_ffn (the pages' first fp9
  * workload was a dense MLP, [fp9]);
  * body pointers 16-byte aligned, sign pointers 2-byte aligned (DUCKMOE_EINVAL).
- * From 3 tokens on, sign planes aligned to 8 bytes (and matrices whose rows
- * are whole multiples of 64 elements) let the kernels fetch more sign bytes
- * per load; other alignments give the same results more slowly.
+ * In the matrix-core kernels (layer calls of 3 tokens and more, prefill),
+ * sign planes aligned to 8 bytes and matrices whose rows are multiples of 64
+ * elements let the kernels fetch more sign bytes per load; other layouts give
+ * the same results more slowly.
  * The struct itself is read on the host during the call only.
  */
 typedef struct duckmoe_layer {
