@@ -371,15 +371,13 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
   const int gw = blockIdx.x * WA + wave;
 #endif
 
-  // A wave whose first task lies in slot 0 (known without the ids) issues its
-  // first weight loads at once; then the ids; then x.
+  // The ids and x first, then a wave whose first task lies in slot 0 (known
+  // without the ids) issues its first weight loads at once.  In that order
+  // the waits for the ids (the plan) and for x (the LDS staging) do not also
+  // wait for those weights (loads complete in issue order).
   GuTile<P> b0, b1;
   GuUnit u0;
   const bool early = gw < NB;
-  if (early) {
-    u0 = gu_unit<P>(a, slot0_expert(a), gw, 0);
-    gu_issue(b0, u0, a, lane);
-  }
   const PlanIn pin = plan_load(a);
   // x rows t0 .. t0 + TG - 1; unconditional buffer loads, zero past each row's end
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)t0 * H, (uint32_t)(TG * H) * 4u);
@@ -390,6 +388,10 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
   float4 xr[XR];
 #pragma unroll
   for (int j = 0; j < XR; ++j) xr[j] = buf_loadf4(rx, x_off(threadIdx.x + j * NT));
+  if (early) {
+    u0 = gu_unit<P>(a, slot0_expert(a), gw, 0);
+    gu_issue(b0, u0, a, lane);
+  }
 
   const WavePlan plan = wave_plan(a, pin);
   if (blockIdx.x == 0 && wave == 0 && t0 == 0) plan_store(plan, a);
