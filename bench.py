@@ -34,8 +34,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "7498e570d89df59925acde65980994e7922971d88bb00103df5240a453a6daf0",
-    "bytes_per_launch": 297756790,
+    "sources_sha256": "12f832b457ec4f47a3ff9b9898413eb227429b92142fc2b071bfd8f69030ce42",
+    "bytes_per_launch": 297756586,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
                   "bit_moe_expert_fp9_amd/csrc/mfma_device.h", "bit_moe_expert_fp9_amd/csrc/host_util.h")
