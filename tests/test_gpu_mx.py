@@ -3,8 +3,8 @@ the random draws of test_gpu_parity.py do not reach: invalid and repeated ids,
 zero routing weights, every token naming the same experts (few slots), every
 id distinct (65 slots at T = 8, top-8: the largest plan, whose last slot the
 down kernel finds in its second word of slot experts), the stage split and
-repeated calls, and each of the three ways the weight tiles load their sign
-bytes.
+repeated calls, each of the three ways the weight tiles load their sign bytes,
+and sign planes moved off 8-byte alignment (the same outputs, bit for bit).
 
 Bars as everywhere: f32 outputs within relative L2 <= 1e-5 and max-abs <=
 1e-4 * max|ref| of the float64 oracle; the status word exact; repeated calls
@@ -175,3 +175,48 @@ def test_stage_split_and_repeat_calls(torch_dev, layer):
     # down again on the same workspace: the same bits
     np.testing.assert_array_equal(dm.moe_down(lay, xd, idd, wd, ws2).cpu().numpy(), first)
     check_close(first, reference(ox, x, ids, w), "T=5")
+
+
+@pytest.mark.parametrize("offset", [2, 4])
+def test_sign_plane_alignment(torch_dev, offset):
+    """The same layer with its sign planes moved 2 or 4 bytes past an 8-byte
+    boundary: the kernels then load the sign bytes as 2-byte or dword words
+    instead of 8-byte pairs, in the bsz 3-8 path and in prefill.  The decoded
+    weights and the arithmetic are the same, so the outputs must be too, bit
+    for bit; the aligned layer is checked against the oracle."""
+    torch = torch_dev
+    wl, H, I, E, K, T = 108, 1024, 512, 16, 4, 6   # even unit counts: 8-byte pairs when aligned
+    say("sign-plane alignment, offset", offset)
+    lay = dm.Layer(H, I, E, K).fill_synthetic(SEED, wl, 0)
+    ox = OracleExperts(SEED, wl, 0, H, I)
+    x = synth.activations(SEED, wl, 0, 50, T, H)
+    ids, w = synth.routing(SEED, wl, 0, 50, T, E, K)
+    xp = synth.activations(SEED, wl, 0, 51, 70, H)
+    idp, wp = synth.routing(SEED, wl, 0, 51, 70, E, K)
+
+    def run():
+        got = dm.moe_layer(lay, to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w)).cpu().numpy()
+        pf = dm.moe_prefill(lay, to_dev(torch, xp), to_dev(torch, idp), to_dev(torch, wp)).cpu().numpy()
+        return got, pf
+
+    aligned = run()
+    planes = []
+    for name in ("gu_sign", "dn_sign"):
+        src = getattr(lay, name)
+        buf = torch.zeros(src.numel() + 16, dtype=torch.uint8, device="cuda")
+        buf[offset:offset + src.numel()].copy_(src)
+        planes.append(buf)
+    saved = (lay.struct.gu_sign, lay.struct.dn_sign)
+    lay.struct.gu_sign = planes[0].data_ptr() + offset
+    lay.struct.dn_sign = planes[1].data_ptr() + offset
+    try:
+        moved = run()
+    finally:
+        lay.struct.gu_sign, lay.struct.dn_sign = saved
+    np.testing.assert_array_equal(moved[0], aligned[0])
+    np.testing.assert_array_equal(moved[1], aligned[1])
+    ox.prefetch([int(i) for i in np.unique(np.concatenate([ids.ravel(), idp.ravel()]))] + [E])
+    check_close(aligned[0], oracle.moe_layer(ox, x, ids, w, E), "aligned layer T=%d" % T)
+    for t in (0, 35, 69):
+        check_close(aligned[1][t], oracle.moe_layer(ox, xp[t:t + 1], idp[t:t + 1], wp[t:t + 1], E)[0],
+                    "aligned prefill token %d" % t)
