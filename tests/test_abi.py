@@ -285,3 +285,15 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(duckmoe, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         duckmoe.quantize_fp9(np.zeros((1, 8), dtype=np.float32))
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says why,
+    before it touches torch or the library."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
