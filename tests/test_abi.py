@@ -67,17 +67,18 @@ def test_workspace_bytes(L):
     lay = fake_layer()
     f = L.duckmoe_workspace_bytes
     # 1 KiB header (status, plan) + h' [T*top_k+1][T][I] f32
-    assert f(ctypes.byref(lay), 1, 1) == 1024 + 9 * 1 * 2048 * 4
-    assert f(ctypes.byref(lay), 2, 32) == 1024 + 17 * 2 * 2048 * 4
+    hdr = 1024
+    assert f(ctypes.byref(lay), 1, 1) == hdr + 9 * 1 * 2048 * 4
+    assert f(ctypes.byref(lay), 2, 32) == hdr + 17 * 2 * 2048 * 4
     assert f(ctypes.byref(lay), 0, 1) == 0
     assert f(ctypes.byref(lay), 9, 1) == 0
     assert f(ctypes.byref(lay), 1, 3) == 0      # 2048 / 3 not integral
     assert f(ctypes.byref(lay), 1, 64) == 0     # slice of 32 < 64
     wide = fake_layer(I=3072)                    # 3 chunks of 1024: no shard partials
-    assert f(ctypes.byref(wide), 1, 1) == 1024 + 9 * 3072 * 4
+    assert f(ctypes.byref(wide), 1, 1) == hdr + 9 * 3072 * 4
     assert f(ctypes.byref(wide), 1, 3) == 0
     dense = fake_layer(I=18432, E=0, k=1)        # a dense MLP: one expert, index 0
-    assert f(ctypes.byref(dense), 1, 1) == 1024 + 2 * 18432 * 4
+    assert f(ctypes.byref(dense), 1, 1) == hdr + 2 * 18432 * 4
     assert f(None, 1, 1) == 0
 
 
