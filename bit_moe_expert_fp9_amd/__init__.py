@@ -22,6 +22,7 @@ from .duckmoe import (  # noqa: F401
     moe_down,
     moe_gate_up,
     moe_layer,
+    moe_layer_noalloc,
     moe_plan,
     moe_prefill,
     moe_stack,

@@ -43,6 +43,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/duckmoe.h"
 #include "fp9_device.h"
@@ -1597,6 +1598,36 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
   return DUCKMOE_OK;
 }
 
+// ------------------------------------------------- allocation-free entry ----
+// The workspace of duckmoe_moe_layer_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  On the host
+// the array's name only stands in for it, so it is never passed to a kernel:
+// its device address is looked up once per device (with that device current)
+// by hipGetSymbolAddress, kept, and passed instead.  Every call on a GPU
+// shares that GPU's array; the layer kernels write everything they read there
+// (plan, status, h'), so nothing has to start at zero.
+static __device__ __align__(256) uint8_t scratch[DUCKMOE_NOALLOC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DUCKMOE_EHIP;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DUCKMOE_EHIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DUCKMOE_OK;
+}
+
 }  // namespace
 }  // namespace duckmoe
 
@@ -1616,6 +1647,16 @@ int duckmoe_moe_layer(const duckmoe_layer *L, const float *x, const int32_t *ids
                       size_t ws_bytes, hipStream_t stream) {
   if (!ids) return DUCKMOE_EINVAL;
   return run_layer(L, x, ids, w, 0, T, out, n_shards, ws, ws_bytes, stream, kBoth);
+}
+
+int duckmoe_moe_layer_noalloc(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                              const float *w, int32_t T, float *out, int32_t n_shards,
+                              hipStream_t stream) {
+  if (!ids) return DUCKMOE_EINVAL;
+  void *ws = nullptr;
+  const int rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  return run_layer(L, x, ids, w, 0, T, out, n_shards, ws, DUCKMOE_NOALLOC_WS_BYTES, stream, kBoth);
 }
 
 int duckmoe_moe_gate_up(const duckmoe_layer *L, const float *x, const int32_t *ids,

@@ -63,6 +63,8 @@ _SIGNATURES = {
     "duckmoe_quantize_fp9": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "duckmoe_workspace_bytes": ([ctypes.POINTER(LayerStruct), _I32, _I32], _SZ),
     "duckmoe_moe_layer": (_LAYER_ARGS, ctypes.c_int),
+    "duckmoe_moe_layer_noalloc": ([ctypes.POINTER(LayerStruct), _P, _P, _P, _I32, _P, _I32, _P],
+                                  ctypes.c_int),
     "duckmoe_moe_gate_up": (_LAYER_ARGS, ctypes.c_int),
     "duckmoe_moe_down": (_LAYER_ARGS, ctypes.c_int),
     "duckmoe_expert_ffn": ([ctypes.POINTER(LayerStruct), _I32, _P, _I32, _P, _I32, _P, _SZ, _P],
@@ -348,6 +350,21 @@ def _layer_call(fname, layer, x, ids, w, out, n_shards, ws, stream):
 def moe_layer(layer, x, ids, w, out=None, n_shards=1, ws=None, stream=None):
     """out = shared(x) + sum_i w[:, i] * expert_{ids[:, i]}(x); device tensors."""
     return _layer_call("duckmoe_moe_layer", layer, x, ids, w, out, n_shards, ws, stream)
+
+
+def moe_layer_noalloc(layer, x, ids, w, out, n_shards=1, stream=None):
+    """moe_layer on the library's static device workspace (no workspace argument);
+    `out` is the caller's ([T, H], or [n_shards, T, H] for shard partials)."""
+    import torch
+    T = x.shape[0]
+    _need_device(x, torch.float32, "x")
+    _need_device(ids, torch.int32, "ids")
+    _need_device(w, torch.float32, "w")
+    _need_device(out, torch.float32, "out")
+    rc = lib().duckmoe_moe_layer_noalloc(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w),
+                                         T, _ptr(out), n_shards, _stream(stream))
+    _check(rc, "duckmoe_moe_layer_noalloc")
+    return out
 
 
 def moe_gate_up(layer, x, ids, w, ws, out=None, n_shards=1, stream=None):

@@ -42,9 +42,12 @@
  *    launched; no output is written then.
  *  - Device entry points are asynchronous on the given stream (0 = the null
  *    stream).  A device fault surfaces at the caller's next synchronisation.
- *  - All memory is caller-owned.  The library allocates nothing and keeps no
- *    mutable global state, so calls on different streams may run concurrently
- *    as long as they use different workspaces and outputs.
+ *  - All memory is caller-owned, except the static device workspace of
+ *    duckmoe_moe_layer_noalloc.  The library allocates no device memory.  Its
+ *    only global state is per-device caches (compute-unit counts, launch
+ *    shapes, that workspace's address), each filled once and then only read,
+ *    so calls on different streams may run concurrently as long as they use
+ *    different workspaces and outputs.
  *  - Device pointers must satisfy the alignment stated for them
  *    (DUCKMOE_EINVAL otherwise).
  */
@@ -194,6 +197,26 @@ size_t duckmoe_workspace_bytes(const duckmoe_layer *L, int32_t T, int32_t n_shar
 int duckmoe_moe_layer(const duckmoe_layer *L, const float *x, const int32_t *ids,
                       const float *w, int32_t T, float *out, int32_t n_shards,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * duckmoe_moe_layer without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call allocates nothing: it runs the
+ * same kernels on a static device array of DUCKMOE_NOALLOC_WS_BYTES bytes that
+ * the library holds on each GPU it runs on until the process ends (its address
+ * is looked up on the first call on a device).  Arguments, results and errors
+ * are those of duckmoe_moe_layer, plus DUCKMOE_EWORKSPACE when the call needs
+ * more than DUCKMOE_NOALLOC_WS_BYTES of workspace (duckmoe_workspace_bytes)
+ * and DUCKMOE_EHIP if the array's address cannot be obtained.  Every call on
+ * one GPU shares that GPU's array, and the array keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams or host
+ * threads) race, so the caller serialises them.  duckmoe_status cannot read
+ * this call's status word (it is in the library's array).
+ */
+#define DUCKMOE_NOALLOC_WS_BYTES (16u << 20)  /* 16 MiB: DeepSeek-V3 layers up to 8 tokens */
+int duckmoe_moe_layer_noalloc(const duckmoe_layer *L, const float *x, const int32_t *ids,
+                              const float *w, int32_t T, float *out, int32_t n_shards,
+                              hipStream_t stream);
 
 /*
  * The two launches duckmoe_moe_layer makes, for callers that time or overlap
