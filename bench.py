@@ -9,9 +9,10 @@ step streams the selected experts from HBM rather than from cache.
 
 Prints one JSON line.  `value` is layer tokens/s at bsz 1 with inputs already
 in HBM.  The roofline object is for the dominant kernel, k_gate_up (two thirds
-of the bytes): a second timed loop launches the two stages of the layer
-separately with HIP events around each, on the stream they run on.  The CPU
-baseline is the float64 oracle on a bounded sample of the same workload.
+of the bytes): its launches run back to back between two HIP events on the
+stream they run on (each on a fresh routing draw), so the average is the
+kernel's own duration plus the gap between two dispatches.  The CPU baseline
+is the float64 oracle on a bounded sample of the same workload.
 """
 
 import argparse
@@ -64,10 +65,10 @@ def parse():
     p.add_argument("--more-bsz", type=str, default="4,8",
                    help="comma-separated further batch sizes (3..8, the matrix-core path) timed "
                         "on the same layer ('' to skip); results go under config.layer_bsz")
-    p.add_argument("--stack", action="store_true",
-                   help="also time the 16-layer stack (about 204 GB of fp9 weights drawn on the "
-                        "device) at bsz 1, 2, 4 and 8; results go under 'stack'")
-    p.add_argument("--stack-steps", type=int, default=100)
+    p.add_argument("--stack", type=int, default=1,
+                   help="time the 16-layer stack (about 204 GB of fp9 weights drawn on the "
+                        "device) at bsz 1, 2, 4 and 8 (0 to skip); results go under 'stack'")
+    p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--dense", type=int, default=1,
                    help="also time the dense fp9 MLP 7168/18432 at bsz 1 and 2 (0 to skip)")
     p.add_argument("--prefill", type=str, default="2048",
@@ -212,6 +213,78 @@ def time_stages(torch, dm, layer, T, steps, warmup, draws):
         "gate_up_gbps": float(gu_bytes.mean() / (gu.mean() * 1e-6) / 1e9),
         "down_gbps": float(dn_bytes.mean() / (dn.mean() * 1e-6) / 1e9),
     }
+
+
+def time_gate_up_back_to_back(torch, dm, layer, T, steps, warmup, draws):
+    """The gate/up stage alone, `steps` launches back to back between two
+    events on their stream, each on a fresh routing draw: the kernel's average
+    duration plus one dispatch gap (no event between launches)."""
+    from bit_moe_expert_fp9_amd import synth
+    n = steps + warmup
+    xs, ids, ws_, uniq = [], [], [], []
+    for s in range(n):
+        d = s % draws
+        xs.append(synth.activations(SEED, WORKLOAD, 0, 70_000 + d, T, H))
+        i, w = synth.routing(SEED, WORKLOAD, 0, 70_000 + d, T, E, K)
+        ids.append(i)
+        ws_.append(w)
+        uniq.append(len(np.unique(i)))
+    X = torch.from_numpy(np.stack(xs)).cuda()
+    IDS = torch.from_numpy(np.stack(ids)).cuda()
+    W = torch.from_numpy(np.stack(ws_)).cuda()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T)
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(steps):
+        s = warmup + k
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    slots = np.array(uniq[warmup:], dtype=np.float64) + 1
+    eb = layer.expert_bytes()
+    gu_bytes = slots * (eb * 2 // 3) + T * H * 4 + slots * T * I * 4
+    return {"us": us, "bytes": float(gu_bytes.mean()),
+            "gbps": float(gu_bytes.mean() / (us * 1e-6) / 1e9)}
+
+
+def time_gemv_256x512(torch, dm, reps=2000):
+    """Workload 1: one fp9 GEMV 256 x 512 (N(0, 0.02) weights, x ~ N(0, 1)) and
+    the decode of all 512 fp9 codes, each as back-to-back launches between two
+    events: launch-bound, reported in microseconds per call."""
+    from bit_moe_expert_fp9_amd import synth
+    Wt = synth.weights(SEED, 1, 0, 0, synth.GATE, (256, 512))
+    body, sign = dm.quantize_fp9(Wt)
+    bd, sd = torch.from_numpy(body).cuda(), torch.from_numpy(sign).cuda()
+    x = torch.from_numpy(synth.activations(SEED, 1, 0, 0, 1, 512)[0]).cuda()
+    y = torch.empty(256, dtype=torch.float32, device="cuda")
+    codes = np.arange(512, dtype=np.uint16)
+    cb = torch.from_numpy((codes & 0xFF).astype(np.uint8)).cuda()
+    cs = torch.from_numpy(np.packbits(((codes >> 8) & 1).astype(np.uint8), bitorder="little")).cuda()
+    dec = torch.empty(512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("gemv_us", lambda: dm.gemv_fp9(bd, sd, x, out=y, stream=stream)),
+                     ("decode_512_codes_us", lambda: dm.decode_fp9(cb, cs, out=dec, stream=stream))):
+        for _ in range(50):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / reps
+    res["what"] = ("256 x 512 fp9 GEMV (147,456 weight bytes) and a decode of all 512 codes, "
+                   "back-to-back launches; launch-bound")
+    log("gemv 256x512:", json.dumps(res))
+    return res
 
 
 def read_ceiling(torch, dm, sizes, reps=100):
@@ -576,6 +649,9 @@ def main():
 
     st1 = time_stages(torch, dm, layer, 1, args.steps, args.warmup, draws)
     log("bsz1 stages:", json.dumps(st1))
+    gu_b2b = time_gate_up_back_to_back(torch, dm, layer, 1, max(args.steps, 50), args.warmup, draws)
+    log("bsz1 gate/up back to back:", json.dumps(gu_b2b))
+    gemv = time_gemv_256x512(torch, dm)
 
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
     pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
@@ -614,6 +690,9 @@ def main():
             "bsz2_hbm_gbps": (r2["bytes_step"] / (r2["ms_per_step"] * 1e-3) / 1e9) if r2 else None,
             "bsz2_ms_per_step": r2["ms_per_step"] if r2 else None,
             "layer_bsz": more or None,
+            "layer_bsz_dtype": "matrix-core path: fp16 weights (exact fp9 decode) times "
+                               "scaled fp16 hi/lo activation pairs, f32 accumulation",
+            "gemv_256x512": gemv,
             "stages_us": {"k_gate_up": st1["gate_up_us"], "k_down": st1["down_us"]},
             "read_ceiling": {"what": "plain streaming read of the same byte count, one launch, "
                                      "fresh window, HIP events (duckmoe_read_probe)",
@@ -629,20 +708,23 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "k_gate_up (gate and up GEMVs + SwiGLU for every selected expert)",
-            "achieved": st1["gate_up_gbps"],
+            "achieved": gu_b2b["gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": st1["gate_up_gbps"] / HBM_PEAK_GBPS,
-            "avg_launch_us": st1["gate_up_us"],
-            "bytes_per_launch": st1["gate_up_bytes"],
+            "frac": gu_b2b["gbps"] / HBM_PEAK_GBPS,
+            "avg_launch_us": gu_b2b["us"],
+            "avg_launch_how": "launches back to back between two HIP events on their stream, "
+                              "fresh routing each",
+            "bytes_per_launch": gu_b2b["bytes"],
             "traffic": measured_traffic(),
             "read_ceiling_gbps": gu_gbps,
-            "frac_of_read_ceiling": st1["gate_up_gbps"] / gu_gbps,
+            "frac_of_read_ceiling": gu_b2b["gbps"] / gu_gbps,
+            "with_events_us": st1["gate_up_us"],
         },
         "cpu_baseline": None,
     }
     if args.stack:
-        res["stack"] = time_stack(torch, dm, args.stack_steps, 10)
+        res["stack"] = time_stack(torch, dm, args.stack_steps, 5)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(res), flush=True)

@@ -1427,14 +1427,12 @@ hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
   const auto kern = k_gate_up<TG, P, WA>;
   const size_t hp = (size_t)((a.H + kChunk - 1) / kChunk) * kChunk;
   const size_t lds = (size_t)TG * hp * sizeof(float);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
+  static OccCache occ;
   int per_cu = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WA * 64, lds);
+  hipError_t err = occupancy(occ, kern, WA * 64, lds, kGuXLds, per_cu);
   if (err != hipSuccess) return err;
   const int cus = device_cus();
-  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  if (cus <= 0) return hipErrorInvalidConfiguration;
   per_cu = std::max(1, std::min(per_cu, DUCKMOE_GU_WAVES_PER_CU / WA));
   hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(WA * 64), lds, st, a, t0);
   return hipGetLastError();
@@ -1445,11 +1443,12 @@ hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
   constexpr int R = down_rows<T>();
   const auto kern = k_down<T, R, kWB>;
   const size_t lds = (size_t)kWB * R * T * 16 * sizeof(float);
+  static OccCache occ;
   int per_cu = 0;
-  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWB * 64, lds);
+  hipError_t err = occupancy(occ, kern, kWB * 64, lds, 0, per_cu);
   if (err != hipSuccess) return err;
   const int cus = device_cus();
-  if (cus <= 0 || per_cu <= 0) return hipErrorInvalidConfiguration;
+  if (cus <= 0) return hipErrorInvalidConfiguration;
   per_cu = std::max(1, std::min(per_cu, DUCKMOE_DN_WAVES_PER_CU / kWB));
   const int nblk = (a.H + R - 1) / R;
   const int grid = std::min(nblk, cus * per_cu);
@@ -1491,8 +1490,9 @@ hipError_t launch_mx_gate_up_sm(const LayerArgs &a, const MxArgs &m, hipStream_t
   constexpr int WA = DUCKMOE_MX_GU_WAVES, RT = DUCKMOE_MX_GU_ROW_TILES;
   const auto kern = k_gate_up_mx<WA, RT, SM>;
   const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
+  static OccCache occ;
   int grid = 0;
-  hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+  hipError_t err = persistent_grid(occ, kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    max_slots * ((a.I + 16 * RT - 1) / (16 * RT)), grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), 0, st, a, m);
@@ -1515,8 +1515,9 @@ template <int SM>
 hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
   constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_DN_ROW_TILES;
   const auto kern = k_down_mx<WA, RT, SM>;
+  static OccCache occ;
   int grid = 0;
-  hipError_t err = persistent_grid(kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
+  hipError_t err = persistent_grid(occ, kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
                                    (a.H + 16 * RT - 1) / (16 * RT) * kMxGroups, grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), 0, st, a, m);
@@ -1608,7 +1609,6 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
 // (plan, status, h'), so nothing has to start at zero.
 static __device__ __align__(256) uint8_t scratch[DUCKMOE_NOALLOC_WS_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::atomic<void *> g_scratch[kMaxDevices];
 std::mutex g_scratch_mu;
 

@@ -133,15 +133,31 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _need_device(t, dtype, name):
-    import torch
-    if t.device.type != "cuda":
+def _need_device(t, dtype, name, shape=None, numel=None, device=None):
+    """Check a tensor argument before its pointer reaches the library: a
+    contiguous device tensor of `dtype`, optionally of exactly `shape`, with at
+    least `numel` elements, on `device`.  Raises ValueError (nothing is launched)."""
+    if t is None:
+        raise ValueError("%s is required" % name)
+    dev = getattr(t, "device", None)
+    if dev is None or dev.type != "cuda":
         raise ValueError("%s must be a device tensor" % name)
+    if device is not None and dev != device:
+        raise ValueError("%s is on %s, the layer's weights on %s" % (name, dev, device))
     if t.dtype != dtype:
-        raise ValueError("%s must be %s" % (name, dtype))
+        raise ValueError("%s must be %s, is %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    del torch
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, has %s" % (name, tuple(shape), tuple(t.shape)))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), numel))
+
+
+def _need_tokens(T, limit=None):
+    limit = MAX_TOKENS if limit is None else limit
+    if not 1 <= T <= limit:
+        raise ValueError("T = %d tokens: must be in [1, %d]" % (T, limit))
 
 
 # ------------------------------------------------------------------ host ----
@@ -174,13 +190,17 @@ def quantize_fp9_device(w, body=None, sign=None, nonfinite=None, stream=None):
     """
     import torch
     _need_device(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
     rows, cols = w.shape
     if body is None:
         body = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
     if sign is None:
         sign = torch.empty((rows, max(cols // 8, 0)), dtype=torch.uint8, device=w.device)
-    if body.numel() < rows * cols or sign.numel() < rows * (cols // 8):
-        raise ValueError("body/sign too small")
+    _need_device(body, torch.uint8, "body", numel=rows * cols, device=w.device)
+    _need_device(sign, torch.uint8, "sign", numel=rows * (cols // 8), device=w.device)
+    if nonfinite is not None:
+        _need_device(nonfinite, torch.int32, "nonfinite", numel=1, device=w.device)
     _check(lib().duckmoe_quantize_fp9_device(_ptr(w), rows, cols, _ptr(body), _ptr(sign),
                                              _ptr(nonfinite), _stream(stream)),
            "duckmoe_quantize_fp9_device")
@@ -193,17 +213,19 @@ def fp8_to_fp9_device(codes, scale, block=128, body=None, sign=None, nonfinite=N
     [ceil(rows/block), ceil(cols/block)] -> (body, sign) fp9 planes on the GPU."""
     import torch
     _need_device(codes, torch.uint8, "codes")
-    _need_device(scale, torch.float32, "scale")
+    if codes.dim() != 2 or block < 1:
+        raise ValueError("codes must be 2-D [rows, cols] and block >= 1")
     rows, cols = codes.shape
     nb = (-(-rows // block), -(-cols // block))
-    if tuple(scale.shape) != nb:
-        raise ValueError("scale grid must be %s" % (nb,))
+    _need_device(scale, torch.float32, "scale", shape=nb, device=codes.device)
     if body is None:
         body = torch.empty((rows, cols), dtype=torch.uint8, device=codes.device)
     if sign is None:
         sign = torch.empty((rows, max(cols // 8, 0)), dtype=torch.uint8, device=codes.device)
-    if body.numel() < rows * cols or sign.numel() < rows * (cols // 8):
-        raise ValueError("body/sign too small")
+    _need_device(body, torch.uint8, "body", numel=rows * cols, device=codes.device)
+    _need_device(sign, torch.uint8, "sign", numel=rows * (cols // 8), device=codes.device)
+    if nonfinite is not None:
+        _need_device(nonfinite, torch.int32, "nonfinite", numel=1, device=codes.device)
     _check(lib().duckmoe_fp8_to_fp9(_ptr(codes), _ptr(scale), rows, cols, block, _ptr(body),
                                     _ptr(sign), _ptr(nonfinite), _stream(stream)),
            "duckmoe_fp8_to_fp9")
@@ -232,6 +254,14 @@ class Layer:
     def n_experts(self):
         return self.n_routed + 1
 
+    @property
+    def device(self):
+        return self.gu_body.device
+
+    def _expert_index(self, e):
+        if not 0 <= e <= self.n_routed:
+            raise ValueError("expert %d: must be in [0, %d]" % (e, self.n_routed))
+
     def expert_bytes(self):
         """fp9 bytes one expert streams (3 matrices, body + sign)."""
         return 3 * self.inter * self.hidden * 9 // 8
@@ -241,6 +271,10 @@ class Layer:
         import torch
         H, I = self.hidden, self.inter
         mat = I * H
+        self._expert_index(e)
+        for a, shp, name in ((gate, (I, H), "gate"), (up, (I, H), "up"), (down, (H, I), "down")):
+            if tuple(np.shape(a)) != shp:
+                raise ValueError("%s must have shape %s" % (name, shp))
         gb, gs = quantize_fp9(np.concatenate([gate, up], axis=0))
         db, dsn = quantize_fp9(down)
         self.gu_body[e * 2 * mat:(e + 1) * 2 * mat].copy_(torch.from_numpy(gb.reshape(-1)))
@@ -253,6 +287,10 @@ class Layer:
         expert e with the device quantizer (asynchronous on `stream`)."""
         H, I = self.hidden, self.inter
         mat = I * H
+        self._expert_index(e)
+        for a, shp, name in ((gate, (I, H), "gate"), (up, (I, H), "up"), (down, (H, I), "down")):
+            if tuple(a.shape) != shp:
+                raise ValueError("%s must have shape %s" % (name, shp))
         for src, rows, body, sign in ((gate, I, self.gu_body[e * 2 * mat:], self.gu_sign[e * 2 * mat // 8:]),
                                       (up, I, self.gu_body[(e * 2 + 1) * mat:],
                                        self.gu_sign[(e * 2 + 1) * mat // 8:]),
@@ -265,6 +303,11 @@ class Layer:
         [H, I], scales on 128 x 128 blocks (see duckmoe_fp8_to_fp9)."""
         H, I = self.hidden, self.inter
         mat = I * H
+        self._expert_index(e)
+        for (codes, _), shp, name in ((gate, (I, H), "gate"), (up, (I, H), "up"),
+                                      (down, (H, I), "down")):
+            if tuple(codes.shape) != shp:
+                raise ValueError("%s codes must have shape %s" % (name, shp))
         for (codes, sc), body, sign in ((gate, self.gu_body[e * 2 * mat:], self.gu_sign[e * 2 * mat // 8:]),
                                         (up, self.gu_body[(e * 2 + 1) * mat:],
                                          self.gu_sign[(e * 2 + 1) * mat // 8:]),
@@ -329,18 +372,39 @@ class Layer:
                            device=self.gu_body.device)
 
 
-def _layer_call(fname, layer, x, ids, w, out, n_shards, ws, stream):
+def _layer_args(layer, x, ids, w, out, n_shards):
+    """Checks shared by the layer calls; returns (T, out)."""
     import torch
+    dev = layer.device
+    _need_device(x, torch.float32, "x", device=dev)
+    if x.dim() != 2 or x.shape[1] != layer.hidden:
+        raise ValueError("x must be [T, %d], is %s" % (layer.hidden, tuple(x.shape)))
     T = x.shape[0]
-    _need_device(x, torch.float32, "x")
+    _need_tokens(T)
     if ids is not None:
-        _need_device(ids, torch.int32, "ids")
-        _need_device(w, torch.float32, "w")
+        _need_device(ids, torch.int32, "ids", shape=(T, layer.top_k), device=dev)
+        _need_device(w, torch.float32, "w", shape=(T, layer.top_k), device=dev)
+    if n_shards < 1:
+        raise ValueError("n_shards must be >= 1")
+    shape = (T, layer.hidden) if n_shards == 1 else (n_shards, T, layer.hidden)
     if out is None:
-        shape = (T, layer.hidden) if n_shards == 1 else (n_shards, T, layer.hidden)
-        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    _need_device(out, torch.float32, "out", numel=n_shards * T * layer.hidden, device=dev)
+    return T, out
+
+
+def _need_ws(ws, nbytes, device):
+    import torch
+    _need_device(ws, torch.uint8, "ws", numel=nbytes, device=device)
+
+
+def _layer_call(fname, layer, x, ids, w, out, n_shards, ws, stream):
+    if ids is None:
+        raise ValueError("ids and w are required")
+    T, out = _layer_args(layer, x, ids, w, out, n_shards)
     if ws is None:
         ws = layer.workspace(T, n_shards)
+    _need_ws(ws, layer.workspace_bytes(T, n_shards), layer.device)
     rc = getattr(lib(), fname)(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w), T,
                                _ptr(out), n_shards, _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, fname)
@@ -355,12 +419,9 @@ def moe_layer(layer, x, ids, w, out=None, n_shards=1, ws=None, stream=None):
 def moe_layer_noalloc(layer, x, ids, w, out, n_shards=1, stream=None):
     """moe_layer on the library's static device workspace (no workspace argument);
     `out` is the caller's ([T, H], or [n_shards, T, H] for shard partials)."""
-    import torch
-    T = x.shape[0]
-    _need_device(x, torch.float32, "x")
-    _need_device(ids, torch.int32, "ids")
-    _need_device(w, torch.float32, "w")
-    _need_device(out, torch.float32, "out")
+    if ids is None or out is None:
+        raise ValueError("ids, w and out are required")
+    T, out = _layer_args(layer, x, ids, w, out, n_shards)
     rc = lib().duckmoe_moe_layer_noalloc(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w),
                                          T, _ptr(out), n_shards, _stream(stream))
     _check(rc, "duckmoe_moe_layer_noalloc")
@@ -376,14 +437,11 @@ def moe_down(layer, x, ids, w, ws, out=None, n_shards=1, stream=None):
 
 
 def expert_ffn(layer, e, x, out=None, n_shards=1, ws=None, stream=None):
-    import torch
-    T = x.shape[0]
-    _need_device(x, torch.float32, "x")
-    if out is None:
-        shape = (T, layer.hidden) if n_shards == 1 else (n_shards, T, layer.hidden)
-        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    layer._expert_index(e)
+    T, out = _layer_args(layer, x, None, None, out, n_shards)
     if ws is None:
         ws = layer.workspace(T, n_shards)
+    _need_ws(ws, layer.workspace_bytes(T, n_shards), layer.device)
     rc = lib().duckmoe_expert_ffn(ctypes.byref(layer.struct), e, _ptr(x), T, _ptr(out),
                                   n_shards, _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "duckmoe_expert_ffn")
@@ -394,17 +452,21 @@ def moe_prefill(layer, x, ids, w, out=None, ws=None, stream=None):
     """The routed layer for many tokens (grouped by expert); ids None runs the
     shared (or only) expert alone."""
     import torch
+    dev = layer.device
+    _need_device(x, torch.float32, "x", device=dev)
+    if x.dim() != 2 or x.shape[1] != layer.hidden:
+        raise ValueError("x must be [T, %d], is %s" % (layer.hidden, tuple(x.shape)))
     T = x.shape[0]
-    _need_device(x, torch.float32, "x")
+    _need_tokens(T, 32768)
     if ids is not None:
-        _need_device(ids, torch.int32, "ids")
-        _need_device(w, torch.float32, "w")
-        if tuple(ids.shape) != (T, layer.top_k) or tuple(w.shape) != (T, layer.top_k):
-            raise ValueError("ids and w must be [T, top_k]")
+        _need_device(ids, torch.int32, "ids", shape=(T, layer.top_k), device=dev)
+        _need_device(w, torch.float32, "w", shape=(T, layer.top_k), device=dev)
     if out is None:
-        out = torch.empty((T, layer.hidden), dtype=torch.float32, device=x.device)
+        out = torch.empty((T, layer.hidden), dtype=torch.float32, device=dev)
+    _need_device(out, torch.float32, "out", numel=T * layer.hidden, device=dev)
     if ws is None:
         ws = layer.prefill_workspace(T, ids is not None)
+    _need_ws(ws, layer.prefill_workspace_bytes(T, ids is not None), dev)
     rc = lib().duckmoe_moe_prefill(ctypes.byref(layer.struct), _ptr(x), _ptr(ids), _ptr(w), T,
                                    _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "duckmoe_moe_prefill")
@@ -415,8 +477,12 @@ def prefill_plan(ids, w, n_routed, stream=None):
     """Device per-expert token lists (test export) -> (offsets, tokens, weights,
     tok_entry, status) as host numpy arrays."""
     import torch
+    _need_device(ids, torch.int32, "ids")
+    if ids.dim() != 2:
+        raise ValueError("ids must be [T, top_k]")
     T, k = ids.shape
     dev = ids.device
+    _need_device(w, torch.float32, "w", shape=(T, k), device=dev)
     offsets = torch.zeros(n_routed + 2, dtype=torch.int32, device=dev)
     tokens = torch.full((T * (k + 1),), -1, dtype=torch.int32, device=dev)
     weights = torch.zeros(T * (k + 1), dtype=torch.float32, device=dev)
@@ -435,9 +501,12 @@ def rms_normalize(x, eps=0.0, out=None, stream=None):
     """y[t] = x[t] / sqrt(mean(x[t]^2) + eps) on the device (x [T, H] float32)."""
     import torch
     _need_device(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
     T, H = x.shape
     if out is None:
         out = torch.empty_like(x)
+    _need_device(out, torch.float32, "out", numel=T * H, device=x.device)
     _check(lib().duckmoe_rms_normalize(_ptr(x), T, H, float(eps), _ptr(out), _stream(stream)),
            "duckmoe_rms_normalize")
     return out
@@ -450,12 +519,16 @@ class Stack:
         self.layers = list(layers)
         self.structs = (LayerStruct * len(self.layers))(*[l.struct for l in self.layers])
 
-    def workspace(self, T):
-        import torch
+    def workspace_bytes(self, T):
         n = lib().duckmoe_stack_workspace_bytes(self.structs, len(self.layers), T)
         if n == 0:
             raise DuckMoeError(EINVAL, "duckmoe_stack_workspace_bytes")
-        return torch.empty(n, dtype=torch.uint8, device=self.layers[0].gu_body.device)
+        return n
+
+    def workspace(self, T):
+        import torch
+        return torch.empty(self.workspace_bytes(T), dtype=torch.uint8,
+                           device=self.layers[0].gu_body.device)
 
 
 def moe_stack(stack, x, ids, w, eps=0.0, out=None, ws=None, stream=None):
@@ -464,14 +537,22 @@ def moe_stack(stack, x, ids, w, eps=0.0, out=None, ws=None, stream=None):
     x [T, H] float32; ids int32 / w float32 [n_layers, T, top_k]; device tensors.
     """
     import torch
-    _need_device(x, torch.float32, "x")
-    _need_device(ids, torch.int32, "ids")
-    _need_device(w, torch.float32, "w")
+    lay = stack.layers[0]
+    dev = lay.device
+    _need_device(x, torch.float32, "x", device=dev)
+    if x.dim() != 2 or x.shape[1] != lay.hidden:
+        raise ValueError("x must be [T, %d], is %s" % (lay.hidden, tuple(x.shape)))
     T = x.shape[0]
+    _need_tokens(T)
+    n = len(stack.layers)
+    _need_device(ids, torch.int32, "ids", shape=(n, T, lay.top_k), device=dev)
+    _need_device(w, torch.float32, "w", shape=(n, T, lay.top_k), device=dev)
     if out is None:
         out = torch.empty_like(x)
+    _need_device(out, torch.float32, "out", numel=T * lay.hidden, device=dev)
     if ws is None:
         ws = stack.workspace(T)
+    _need_ws(ws, stack.workspace_bytes(T), dev)
     _check(lib().duckmoe_moe_stack(stack.structs, len(stack.layers), _ptr(x), _ptr(ids), _ptr(w),
                                    T, float(eps), _ptr(out), _ptr(ws), ws.numel(),
                                    _stream(stream)), "duckmoe_moe_stack")
@@ -480,18 +561,32 @@ def moe_stack(stack, x, ids, w, eps=0.0, out=None, ws=None, stream=None):
 
 def read_probe(buf, nbytes, sink, stream=None):
     """Plain streaming read of the first nbytes of device tensor buf (calibration)."""
+    import torch
+    _need_device(buf, buf.dtype if buf is not None else None, "buf")
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes %d exceeds buf's %d bytes" % (nbytes, buf.numel() * buf.element_size()))
+    _need_device(sink, torch.int32, "sink", numel=1, device=buf.device)
     _check(lib().duckmoe_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
            "duckmoe_read_probe")
 
 
 class Lane:
     """An asynchronous lane: its own stream (default priority), workspace and
-    events (see duckmoe_lane_* in the header)."""
+    events (see duckmoe_lane_* in the header).
+
+    The tensors handed to begin are recorded on the lane's stream
+    (Tensor.record_stream), so torch's caching allocator does not give their
+    memory to new tensors before the lane's kernels have read and written
+    them, even if the caller drops them right after begin.  close() waits for
+    the lane's last layer before it releases the workspace and the events.
+    """
 
     def __init__(self, layer, max_tokens=1):
         import torch
+        self.max_tokens = max_tokens
         self.stream = torch.cuda.Stream(device=layer.gu_body.device)
         self.ws = layer.workspace(max_tokens)
+        self.ws.record_stream(self.stream)
         self.struct = LaneStruct(self.stream.cuda_stream, self.ws.data_ptr(), self.ws.numel(),
                                  None, None)
         _check(lib().duckmoe_lane_init(ctypes.byref(self.struct)), "duckmoe_lane_init")
@@ -499,14 +594,17 @@ class Lane:
     def begin(self, layer, x, ids, w, out, producer=None):
         """Start the layer for this lane once `producer` (default: the current
         stream) has produced x, ids and w; returns at once."""
-        import torch
-        _need_device(x, torch.float32, "x")
-        _need_device(ids, torch.int32, "ids")
-        _need_device(w, torch.float32, "w")
-        _need_device(out, torch.float32, "out")
+        if ids is None or out is None:
+            raise ValueError("ids, w and out are required")
+        T, out = _layer_args(layer, x, ids, w, out, 1)
+        _need_tokens(T, self.max_tokens)
+        if self.ws is None:
+            raise ValueError("the lane is closed")
         _check(lib().duckmoe_lane_begin(ctypes.byref(self.struct), ctypes.byref(layer.struct),
-                                        _ptr(x), _ptr(ids), _ptr(w), x.shape[0], _ptr(out),
+                                        _ptr(x), _ptr(ids), _ptr(w), T, _ptr(out),
                                         _stream(producer)), "duckmoe_lane_begin")
+        for t in (x, ids, w, out):
+            t.record_stream(self.stream)
 
     def finish(self, consumer=None, block=False):
         """Make `consumer` (default: the current stream) wait for the lane's
@@ -516,7 +614,10 @@ class Lane:
 
     def close(self):
         if self.struct.done or self.struct.ready:
+            # the lane's kernels may still use the workspace: wait for them first
+            self.stream.synchronize()
             _check(lib().duckmoe_lane_destroy(ctypes.byref(self.struct)), "duckmoe_lane_destroy")
+        self.ws = None
 
     def __del__(self):
         try:
@@ -526,6 +627,8 @@ class Lane:
 
 
 def status(ws, stream=None):
+    import torch
+    _need_device(ws, torch.uint8, "ws", numel=8)
     st = _I32(0)
     _check(lib().duckmoe_status(_ptr(ws), ctypes.byref(st), _stream(stream)), "duckmoe_status")
     return st.value
@@ -536,9 +639,14 @@ def status(ws, stream=None):
 def decode_fp9(body, sign, n=None, out=None, stream=None):
     """Device decode of fp9 planes to float32 (test export)."""
     import torch
+    _need_device(body, torch.uint8, "body")
     n = body.numel() if n is None else n
+    if not 0 <= n <= body.numel():
+        raise ValueError("n = %d: body holds %d codes" % (n, body.numel()))
+    _need_device(sign, torch.uint8, "sign", numel=(n + 7) // 8, device=body.device)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=body.device)
+    _need_device(out, torch.float32, "out", numel=n, device=body.device)
     _check(lib().duckmoe_decode_fp9(_ptr(body), _ptr(sign), n, _ptr(out), _stream(stream)),
            "duckmoe_decode_fp9")
     return out
@@ -547,9 +655,15 @@ def decode_fp9(body, sign, n=None, out=None, stream=None):
 def gemv_fp9(body, sign, x, out=None, stream=None):
     """y = W x with W in fp9 planes body [rows, cols], sign [rows, cols/8]."""
     import torch
+    _need_device(body, torch.uint8, "body")
+    if body.dim() != 2:
+        raise ValueError("body must be 2-D [rows, cols]")
     rows, cols = body.shape
+    _need_device(sign, torch.uint8, "sign", numel=rows * (cols // 8), device=body.device)
+    _need_device(x, torch.float32, "x", numel=cols, device=body.device)
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=body.device)
+    _need_device(out, torch.float32, "out", numel=rows, device=body.device)
     _check(lib().duckmoe_gemv_fp9(_ptr(body), _ptr(sign), rows, cols, _ptr(x), _ptr(out),
                                   _stream(stream)), "duckmoe_gemv_fp9")
     return out
@@ -559,6 +673,9 @@ def moe_plan(ids, n_routed, stream=None):
     """Device expert-selection plan -> expert indices in slot order (shared
     first, then the distinct valid ids by first appearance)."""
     import torch
+    _need_device(ids, torch.int32, "ids")
+    if ids.dim() != 2:
+        raise ValueError("ids must be [T, top_k]")
     T, k = ids.shape
     uniq = torch.full((T * k + 1,), -1, dtype=torch.int32, device=ids.device)
     n = torch.zeros(1, dtype=torch.int32, device=ids.device)

@@ -120,9 +120,12 @@ def test_full_size_pair_as_two_lanes(torch_dev):
     ids, w = synth.routing(SEED, wl, 0, 7, 2, E, K)
     lanes = [dm.Lane(lay), dm.Lane(lay)]
     outs = [torch.empty((1, H), device="cuda") for _ in lanes]
+    # the device inputs stay referenced until the lanes finish
+    xs = [to_dev(torch, x[t:t + 1]) for t in range(2)]
+    idss = [to_dev(torch, ids[t:t + 1]) for t in range(2)]
+    wss = [to_dev(torch, w[t:t + 1]) for t in range(2)]
     for t in range(2):
-        lanes[t].begin(lay, to_dev(torch, x[t:t + 1]), to_dev(torch, ids[t:t + 1]),
-                       to_dev(torch, w[t:t + 1]), outs[t])
+        lanes[t].begin(lay, xs[t], idss[t], wss[t], outs[t])
     for lane in lanes:
         lane.finish()
     got = torch.cat(outs).cpu().numpy()

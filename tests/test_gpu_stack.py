@@ -227,7 +227,7 @@ def full_stack(torch_dev):
 @pytest.mark.parametrize("T,samples", [
     (1, [(0, [0]), (15, [0])]),
     (2, [(9, [0, 1])]),
-    (4, []),
+    (4, [(6, [3])]),
     (8, [(12, [5])]),
 ])
 def test_full_stack(torch_dev, full_stack, T, samples):
