@@ -327,7 +327,7 @@ def time_pair(torch, dm, layer, steps, warmup, draws):
     out2 = torch.empty((2, H), dtype=torch.float32, device="cuda")
     outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in range(2)]
     ws1, ws2 = layer.workspace(1), layer.workspace(2)
-    lanes = [dm.Lane(layer), dm.Lane(layer)]
+    lanes = []  # created after the two single-stream forms are timed
 
     def bsz2(s):
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out2, ws=ws2, stream=stream)
@@ -345,7 +345,15 @@ def time_pair(torch, dm, layer, steps, warmup, draws):
                          ws=ws1, stream=stream)
 
     res = {}
-    for name, fn in (("bsz2_call", bsz2), ("two_lanes", lanes2), ("two_serial_calls", serial)):
+    n_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    for name, fn in (("bsz2_call", bsz2), ("two_serial_calls", serial), ("two_lanes", lanes2),
+                     ("two_lanes_half_budget", lanes2)):
+        for lane in lanes:
+            lane.close()
+        if name == "two_lanes":
+            lanes[:] = [dm.Lane(layer), dm.Lane(layer)]
+        elif name == "two_lanes_half_budget":
+            lanes[:] = [dm.Lane(layer, cus=n_cus // 2) for _ in range(2)]
         for s in range(warmup):
             fn(s)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -360,6 +368,102 @@ def time_pair(torch, dm, layer, steps, warmup, draws):
     for lane in lanes:
         lane.close()
     log("pair:", json.dumps(res))
+    return res
+
+
+def time_lane_overlap(torch, dm, layer, steps, warmup, draws):
+    """The pair runtime of the pages' dual-lane decode on one GPU: per decoder
+    layer each of two lanes runs a GPU stage (a bf16 GEMM stands in for the
+    attention part, 1024 x 7168 by 7168 x 4096) and then the MoE layer (bsz 1),
+    the next stage of a lane waiting for its MoE.  Serial: everything on one
+    stream.  Overlapped: the stages on a stream of their own and each lane's
+    MoE on its lane stream, so one lane's MoE runs while the other lane's
+    stage does; with lanes sized to half the CUs, and (for comparison) with
+    lanes whose grids fill the device."""
+    from bit_moe_expert_fp9_amd import synth
+    n = steps + warmup
+    X = torch.from_numpy(np.stack([synth.activations(SEED, WORKLOAD, 0, 80_000 + s % draws, 2, H)
+                                   for s in range(n)])).cuda()
+    r = [synth.routing(SEED, WORKLOAD, 0, 80_000 + s % draws, 2, E, K) for s in range(n)]
+    IDS = torch.from_numpy(np.stack([a for a, _ in r])).cuda()
+    W = torch.from_numpy(np.stack([b for _, b in r])).cuda()
+    ga = torch.randn(1024, 7168, device="cuda", dtype=torch.bfloat16)
+    gb = torch.randn(7168, 4096, device="cuda", dtype=torch.bfloat16)
+    gc = [torch.empty(1024, 4096, device="cuda", dtype=torch.bfloat16) for _ in range(2)]
+    outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    ws1 = layer.workspace(1)
+
+    def stage(t, st):
+        with torch.cuda.stream(st):
+            torch.matmul(ga, gb, out=gc[t])
+
+    # GPU stage and MoE alone, each back to back on the whole device
+    for _ in range(5):
+        stage(0, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        stage(0, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    stage_us = a.elapsed_time(b) * 1e3 / steps
+
+    def serial(s):
+        for t in range(2):
+            stage(t, stream)
+            dm.moe_layer(layer, X[s][t:t + 1], IDS[s][t:t + 1], W[s][t:t + 1], out=outs[t],
+                         ws=ws1, stream=stream)
+
+    for s in range(warmup):
+        serial(s)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(steps):
+        serial(warmup + k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    serial_us = a.elapsed_time(b) * 1e3 / steps
+
+    def run_overlapped(sst, lanes):
+        def overlapped(s):
+            for t in range(2):
+                lanes[t].finish(consumer=sst)   # this lane's previous MoE is done
+                stage(t, sst)
+                lanes[t].begin(layer, X[s][t:t + 1], IDS[s][t:t + 1], W[s][t:t + 1], outs[t],
+                               producer=sst)
+
+        torch.cuda.synchronize()
+        for s in range(warmup):
+            overlapped(s)
+        for lane in lanes:
+            lane.finish(consumer=sst)
+        sst.synchronize()
+        a.record(sst)
+        for k in range(steps):
+            overlapped(warmup + k)
+        for lane in lanes:
+            lane.finish(consumer=sst)
+        b.record(sst)
+        sst.synchronize()
+        for lane in lanes:
+            lane.close()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    n_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    over_full_us = run_overlapped(torch.cuda.Stream(), [dm.Lane(layer), dm.Lane(layer)])
+    over_us = run_overlapped(torch.cuda.Stream(),
+                             [dm.Lane(layer, cus=n_cus // 2), dm.Lane(layer, cus=n_cus // 2)])
+    res = {"what": "per decoder layer, two lanes: GPU stage (bf16 GEMM 1024x7168x4096) then "
+                   "the bsz-1 MoE layer, the next stage of a lane after its MoE; serial = one "
+                   "stream; overlapped = the stages on their own stream, each lane's MoE on "
+                   "its lane stream with a CU budget of half the device, so one lane's MoE "
+                   "runs while the other lane's stage does",
+           "stage_us": stage_us, "serial_us_per_layer": serial_us,
+           "overlapped_us_per_layer": over_us, "speedup": serial_us / over_us,
+           "overlapped_full_grid_lanes_us_per_layer": over_full_us}
+    log("lane overlap:", json.dumps(res))
     return res
 
 
@@ -655,6 +759,7 @@ def main():
 
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
     pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
+    overlap = time_lane_overlap(torch, dm, layer, min(args.steps, 100), 10, draws)
     extra = time_expert_and_partials(torch, dm, layer, min(args.steps, 300), 20)
     prefill = {}
     for tok in [int(v) for v in args.prefill.split(",") if v.strip()]:
@@ -701,6 +806,7 @@ def main():
             "layer_frac_of_read_ceiling": gbps / lay_gbps,
             "dense_mlp": dense,
             "pair_two_tokens": pair,
+            "lane_overlap": overlap,
             "expert_and_partials": extra,
             "prefill": prefill or None,
             "k_down_gbps": st1["down_gbps"],

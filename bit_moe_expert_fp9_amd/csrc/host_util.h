@@ -71,15 +71,23 @@ hipError_t occupancy(OccCache &c, K kern, int threads, size_t lds, size_t attr_l
   return hipSuccess;
 }
 
+// CUs a launch may use: the device's, or fewer when the caller runs on a
+// stream limited to a CU subset (budget > 0: that many CUs).
+inline int cu_budget(int budget) {
+  const int cus = device_cus();
+  return (budget > 0 && cus > 0) ? std::min(budget, cus) : cus;
+}
+
 // Grid of a persistent kernel: resident workgroups per CU from the occupancy
-// API (at most waves_per_cu waves per CU), times the CUs, capped at `cap`.
+// API (at most waves_per_cu waves per CU), times the CUs it may use (budget,
+// see cu_budget), capped at `cap`.
 template <typename K>
 hipError_t persistent_grid(OccCache &c, K kern, int threads, int waves_per_cu, int cap,
-                           int &grid) {
+                           int budget, int &grid) {
   int per_cu = 0;
   hipError_t err = occupancy(c, kern, threads, 0, 0, per_cu);
   if (err != hipSuccess) return err;
-  const int cus = device_cus();
+  const int cus = cu_budget(budget);
   if (cus <= 0) return hipErrorInvalidConfiguration;
   per_cu = std::max(1, std::min(per_cu, waves_per_cu / (threads / 64)));
   grid = std::max(1, std::min(cus * per_cu, cap));

@@ -747,7 +747,8 @@ hipError_t launch_pf_gemm(const PfArgs &a, int max_tiles, hipStream_t stream) {
   int grid = 0;
   const int NB = ((GU ? a.I : a.H) + pf_rows<RT>() - 1) / pf_rows<RT>();
   static OccCache occ;
-  const hipError_t err = persistent_grid(occ, kern, threads, WGCU * kPfWaves, max_tiles * NB, grid);
+  const hipError_t err = persistent_grid(occ, kern, threads, WGCU * kPfWaves, max_tiles * NB, 0,
+                                         grid);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, stream, a);
   return hipSuccess;

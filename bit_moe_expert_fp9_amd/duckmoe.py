@@ -49,6 +49,7 @@ class LaneStruct(ctypes.Structure):
         ("ws_bytes", ctypes.c_size_t),
         ("ready", ctypes.c_void_p),
         ("done", ctypes.c_void_p),
+        ("cus", ctypes.c_int32),
     ]
 
 
@@ -574,6 +575,11 @@ class Lane:
     """An asynchronous lane: its own stream (default priority), workspace and
     events (see duckmoe_lane_* in the header).
 
+    cus (> 0) gives the lane a CU budget: its persistent grids are sized to
+    that many CUs, so two lanes with half the device each fill it once
+    between them and run side by side (by default each lane's grids fill the
+    whole device, and two lanes at once wait for each other's workgroups).
+
     The tensors handed to begin are recorded on the lane's stream
     (Tensor.record_stream), so torch's caching allocator does not give their
     memory to new tensors before the lane's kernels have read and written
@@ -581,15 +587,20 @@ class Lane:
     the lane's last layer before it releases the workspace and the events.
     """
 
-    def __init__(self, layer, max_tokens=1):
+    def __init__(self, layer, max_tokens=1, cus=0):
         import torch
         self.max_tokens = max_tokens
         self.stream = torch.cuda.Stream(device=layer.gu_body.device)
         self.ws = layer.workspace(max_tokens)
         self.ws.record_stream(self.stream)
         self.struct = LaneStruct(self.stream.cuda_stream, self.ws.data_ptr(), self.ws.numel(),
-                                 None, None)
+                                 None, None, int(cus))
         _check(lib().duckmoe_lane_init(ctypes.byref(self.struct)), "duckmoe_lane_init")
+
+    @property
+    def cus(self):
+        """CUs the lane's kernels may use (0: the whole device)."""
+        return self.struct.cus
 
     def begin(self, layer, x, ids, w, out, producer=None):
         """Start the layer for this lane once `producer` (default: the current

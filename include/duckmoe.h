@@ -328,7 +328,16 @@ int duckmoe_prefill_plan(const int32_t *ids, const float *w, int32_t T, int32_t 
  * while other work runs on the caller's streams.  The struct is caller-owned;
  * duckmoe_lane_init fills the events (no device memory is allocated) and
  * duckmoe_lane_destroy releases them.
- *   stream    the lane's stream (created by the caller, default priority)
+ *   stream    the lane's stream (created by the caller, default priority).  A
+ *             stream limited to a CU subset (hipExtStreamCreateWithCUMask)
+ *             keeps the lane's kernels there: two lanes on complementary
+ *             halves of the CUs run side by side instead of each filling the
+ *             whole device and waiting for the other's workgroups.  Without
+ *             a mask, a CU budget in `cus` (say half the device for each of
+ *             two lanes) sizes each lane's persistent grids so that the two
+ *             together fill the device once.  The results do not depend on
+ *             the CU count (each output is computed in the same order on any
+ *             grid).
  *   ws        the lane's workspace: >= duckmoe_workspace_bytes(L, T, 1) for the
  *             largest T it will run, 256-byte aligned; one lane per workspace
  * duckmoe_lane_begin records an event on `producer` (the stream that wrote x,
@@ -347,6 +356,10 @@ typedef struct duckmoe_lane {
   size_t ws_bytes;
   hipEvent_t ready;  /* set by duckmoe_lane_init */
   hipEvent_t done;   /* set by duckmoe_lane_init */
+  int32_t cus;       /* CUs the lane's launches size their grids to (0 = all).  Set
+                        by the caller before duckmoe_lane_init as a budget, or 0;
+                        lane_init caps it by the stream's CU mask (or takes the
+                        mask's count when it is 0) */
 } duckmoe_lane;
 
 int duckmoe_lane_init(duckmoe_lane *lane);

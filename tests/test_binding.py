@@ -203,7 +203,7 @@ def test_lane_begin_records_streams(fake_lib):
     lane.max_tokens = 1
     lane.stream = FakeStream()
     lane.ws = FakeTensor((lay.workspace_bytes(1),), torch.uint8)
-    lane.struct = dmm.LaneStruct(0, 0, 0, None, None)
+    lane.struct = dmm.LaneStruct(0, 0, 0, None, None, 0)
     x, ids, w = (FakeTensor((1, H), torch.float32), FakeTensor((1, K), torch.int32),
                  FakeTensor((1, K), torch.float32))
     out = FakeTensor((1, H), torch.float32)

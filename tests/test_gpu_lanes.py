@@ -135,3 +135,33 @@ def test_full_size_pair_as_two_lanes(torch_dev):
     check_close(got, oracle.moe_layer(ox, x, ids, w, E), "two lanes vs oracle")
     for lane in lanes:
         lane.close()
+
+
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_lanes_on_cu_halves(torch_dev, small, T):
+    """Two lanes with a CU budget of half the device each: each lane sizes its
+    grids to half the CUs and still gives the plain call's outputs bit for bit
+    (vector path at T <= 2, matrix cores at 5)."""
+    torch = torch_dev
+    lay, _, wl = small
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("lanes on half the CUs each, T =", T, "of", n_cus, "CUs")
+    lanes = [dm.Lane(lay, max_tokens=T, cus=n_cus // 2) for _ in range(2)]
+    for lane in lanes:
+        assert lane.cus == n_cus // 2, lane.cus
+    cases = []
+    for s in (3, 4):
+        x = synth.activations(SEED, wl, 0, 40 + 10 * T + s, T, lay.hidden)
+        ids, w = synth.routing(SEED, wl, 0, 40 + 10 * T + s, T, lay.n_routed, lay.top_k)
+        cases.append((to_dev(torch, x), to_dev(torch, ids), to_dev(torch, w)))
+    ref = [dm.moe_layer(lay, *c).cpu().numpy() for c in cases]
+    outs = [torch.full((T, lay.hidden), float("nan"), device="cuda") for _ in lanes]
+    for rep in range(3):
+        for lane, c, o in zip(lanes, cases, outs):
+            lane.begin(lay, *c, o)
+        for lane in lanes:
+            lane.finish(block=True)
+        for o, r in zip(outs, ref):
+            np.testing.assert_array_equal(o.cpu().numpy(), r)
+    for lane in lanes:
+        lane.close()
