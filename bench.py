@@ -35,8 +35,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "12f832b457ec4f47a3ff9b9898413eb227429b92142fc2b071bfd8f69030ce42",
-    "bytes_per_launch": 297756586,
+    "sources_sha256": "f5f4ba6a185f786614dd55fa8b08acc9a9de15f01187a082779450b0830b965e",
+    "bytes_per_launch": 297748229,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
                   "bit_moe_expert_fp9_amd/csrc/mfma_device.h", "bit_moe_expert_fp9_amd/csrc/host_util.h")
@@ -75,6 +75,9 @@ def parse():
                    help="comma-separated token counts for the prefill path on the same layer "
                         "('' to skip); results go under config.prefill")
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--extra", type=int, default=1,
+                   help="also run the 256x512 GEMV, lane-overlap, single-expert and shard-partial "
+                        "legs (0 to skip)")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="first run 3 plain device copies of this many MiB (a known-size "
                         "reference for HBM byte counters under rocprofv3 --pmc)")
@@ -755,12 +758,12 @@ def main():
     log("bsz1 stages:", json.dumps(st1))
     gu_b2b = time_gate_up_back_to_back(torch, dm, layer, 1, max(args.steps, 50), args.warmup, draws)
     log("bsz1 gate/up back to back:", json.dumps(gu_b2b))
-    gemv = time_gemv_256x512(torch, dm)
+    gemv = time_gemv_256x512(torch, dm) if args.extra else None
 
     dense = time_dense(torch, dm, min(args.steps, 300), 20) if args.dense else None
     pair = time_pair(torch, dm, layer, min(args.steps, 300), 20, draws) if args.bsz2 else None
-    overlap = time_lane_overlap(torch, dm, layer, min(args.steps, 100), 10, draws)
-    extra = time_expert_and_partials(torch, dm, layer, min(args.steps, 300), 20)
+    overlap = time_lane_overlap(torch, dm, layer, min(args.steps, 100), 10, draws) if args.extra else None
+    extra = time_expert_and_partials(torch, dm, layer, min(args.steps, 300), 20) if args.extra else None
     prefill = {}
     for tok in [int(v) for v in args.prefill.split(",") if v.strip()]:
         prefill[str(tok)] = time_prefill(torch, dm, layer, tok, args.prefill_steps, 3)
