@@ -98,6 +98,72 @@ def calib_copy(torch, mib):
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
+SETTLE_MS = 60.0
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Runs fn() untimed, synchronizing every few calls, until `ms` of wall time
+    has passed.  After a pause (the host preparing the next measurement's
+    inputs) the GPU's clocks take tens of milliseconds to come back up:
+    measured on MI355X, bsz-2 layer calls right after a 50 ms pause ran about
+    11% slower over the next 20 calls than after 50 ms of work, and needed
+    some 30 ms of calls to recover.  Every timed region starts settled."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
+def back_to_back_us(torch, stream, steps, call, primer):
+    """Mean microseconds per call of `call(k)`, k = 0 .. steps-1, launched back
+    to back between two events on `stream`, after settle() with `primer`.
+    `primer()`, an untimed call of the same kind, is queued just ahead of the
+    start event: the GPU runs it while
+    the host queues the first timed calls, so the start event does not wait on
+    the host's first launch (some tens of microseconds of Python and launch
+    work, which over 20 steps would add more than a microsecond per step)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(torch, primer)
+    primer()
+    a.record(stream)
+    for k in range(steps):
+        call(k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+
+def graph_us(torch, call, n=64, replays=5):
+    """Mean microseconds per call of `call(k, stream)`, k = 0 .. n-1, captured in
+    one HIP graph and replayed back to back between two events: the GPU's own
+    time per call, with no host work between launches (the calls launch
+    kernels only).  One replay, queued ahead of the start event, is untimed."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0, side)  # each launch site's first call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for k in range(n):
+            call(k, st)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(torch, g.replay)
+    g.replay()
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (n * replays)
+    del g
+    return us
+
 
 def time_layer(torch, dm, layer, T, steps, warmup, draws):
     """Times `steps` layer calls (after `warmup`): once back to back between two
@@ -125,18 +191,19 @@ def time_layer(torch, dm, layer, T, steps, warmup, draws):
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
     torch.cuda.synchronize()
 
-    # The timed region: `steps` calls back to back between two events.
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    a.record(stream)
-    for k in range(steps):
+    # The timed region: `steps` calls back to back between two events, the
+    # last warm-up draw queued ahead of the start event as the primer.
+    def call(k):
         s = warmup + k
         dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
+
+    def primer():
+        s = max(warmup - 1, 0)
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+
+    t0 = time.perf_counter()
+    total_ms = back_to_back_us(torch, stream, steps, call, primer) * steps / 1e3
     wall = time.perf_counter() - t0
-    total_ms = a.elapsed_time(b)
     # The per-call distribution: the same calls again with an event before each
     # (an event between two calls adds its own gap, so this pass is not the
     # throughput figure).
@@ -185,10 +252,13 @@ def time_stages(torch, dm, layer, T, steps, warmup, draws):
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = layer.workspace(T)
     stream = torch.cuda.current_stream()
-    for s in range(warmup):
+    def both(s):
         dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
         dm.moe_down(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
-    torch.cuda.synchronize()
+
+    for s in range(warmup):
+        both(s)
+    settle(torch, lambda: both(max(warmup - 1, 0)))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     for k in range(steps):
         s = warmup + k
@@ -240,15 +310,15 @@ def time_gate_up_back_to_back(torch, dm, layer, T, steps, warmup, draws):
     stream = torch.cuda.current_stream()
     for s in range(warmup):
         dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for k in range(steps):
+    def call(k):
         s = warmup + k
         dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / steps
+
+    def primer():
+        s = max(warmup - 1, 0)
+        dm.moe_gate_up(layer, X[s], IDS[s], W[s], ws, out=out, stream=stream)
+
+    us = back_to_back_us(torch, stream, steps, call, primer)
     slots = np.array(uniq[warmup:], dtype=np.float64) + 1
     eb = layer.expert_bytes()
     gu_bytes = slots * (eb * 2 // 3) + T * H * 4 + slots * T * I * 4
@@ -272,20 +342,29 @@ def time_gemv_256x512(torch, dm, reps=2000):
     dec = torch.empty(512, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     res = {}
+
+    def fn_st(name, st):
+        if name == "gemv_us":
+            dm.gemv_fp9(bd, sd, x, out=y, stream=st)
+        else:
+            dm.decode_fp9(cb, cs, out=dec, stream=st)
+
     for name, fn in (("gemv_us", lambda: dm.gemv_fp9(bd, sd, x, out=y, stream=stream)),
                      ("decode_512_codes_us", lambda: dm.decode_fp9(cb, cs, out=dec, stream=stream))):
         for _ in range(50):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        settle(torch, fn)
         a.record(stream)
         for _ in range(reps):
             fn()
         b.record(stream)
         torch.cuda.synchronize()
         res[name] = a.elapsed_time(b) * 1e3 / reps
-    res["what"] = ("256 x 512 fp9 GEMV (147,456 weight bytes) and a decode of all 512 codes, "
-                   "back-to-back launches; launch-bound")
+        res[name.replace("_us", "_graph_us")] = graph_us(torch, lambda k, st: fn_st(name, st))
+    res["what"] = ("256 x 512 fp9 GEMV (147,456 weight bytes) and a decode of all 512 codes: "
+                   "back-to-back launches from the host (bound by the host's launch work), "
+                   "and the same launches replayed from a HIP graph (*_graph_us)")
     log("gemv 256x512:", json.dumps(res))
     return res
 
@@ -303,7 +382,7 @@ def read_ceiling(torch, dm, sizes, reps=100):
         for i in range(10):
             dm.read_probe(buf[(i % 8) * win:], nb, sink, stream=stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
-        torch.cuda.synchronize()
+        settle(torch, lambda: dm.read_probe(buf[5 * win:], nb, sink, stream=stream))
         for i in range(reps):
             ev[2 * i].record(stream)
             dm.read_probe(buf[((i * 3) % 8) * win:], nb, sink, stream=stream)
@@ -359,14 +438,8 @@ def time_pair(torch, dm, layer, steps, warmup, draws):
             lanes[:] = [dm.Lane(layer, cus=n_cus // 2) for _ in range(2)]
         for s in range(warmup):
             fn(s)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for k in range(steps):
-            fn(warmup + k)
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / steps
+        us = back_to_back_us(torch, stream, steps, lambda k: fn(warmup + k),
+                             lambda: fn(max(warmup - 1, 0)))
         res[name] = {"us_per_pair": us, "tokens_per_s": 2 / (us * 1e-6)}
     for lane in lanes:
         lane.close()
@@ -404,14 +477,8 @@ def time_lane_overlap(torch, dm, layer, steps, warmup, draws):
     # GPU stage and MoE alone, each back to back on the whole device
     for _ in range(5):
         stage(0, stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(steps):
-        stage(0, stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    stage_us = a.elapsed_time(b) * 1e3 / steps
+    stage_us = back_to_back_us(torch, stream, steps, lambda k: stage(0, stream),
+                               lambda: stage(0, stream))
 
     def serial(s):
         for t in range(2):
@@ -421,13 +488,9 @@ def time_lane_overlap(torch, dm, layer, steps, warmup, draws):
 
     for s in range(warmup):
         serial(s)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for k in range(steps):
-        serial(warmup + k)
-    b.record(stream)
-    torch.cuda.synchronize()
-    serial_us = a.elapsed_time(b) * 1e3 / steps
+    serial_us = back_to_back_us(torch, stream, steps, lambda k: serial(warmup + k),
+                                lambda: serial(max(warmup - 1, 0)))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def run_overlapped(sst, lanes):
         def overlapped(s):
@@ -440,6 +503,7 @@ def time_lane_overlap(torch, dm, layer, steps, warmup, draws):
         torch.cuda.synchronize()
         for s in range(warmup):
             overlapped(s)
+        settle(torch, lambda: overlapped(max(warmup - 1, 0)))
         for lane in lanes:
             lane.finish(consumer=sst)
         sst.synchronize()
@@ -481,16 +545,32 @@ def time_expert_and_partials(torch, dm, layer, steps, warmup):
     e = 17
     for _ in range(warmup):
         dm.expert_ffn(layer, e, x1, out=out1, ws=ws1, stream=stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for k in range(steps):  # a different expert each call, so HBM is read
+
+    def one(k):  # a different expert each call, so HBM is read
         dm.expert_ffn(layer, k % E, x1, out=out1, ws=ws1, stream=stream)
-    b.record(stream)
+
+    us = back_to_back_us(torch, stream, steps, one, lambda: one(E - 1))
+    t0 = time.perf_counter()  # the host's own time per call: the enqueue loop alone
+    for k in range(steps):
+        one(k)
+    host_us = (time.perf_counter() - t0) * 1e6 / steps
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / steps
     eb = layer.expert_bytes()
-    res["one_expert_bsz1"] = {"us": us, "hbm_gbps": eb / (us * 1e-6) / 1e9, "bytes": eb}
+    # host_us_per_call: the host's time per call over the same loop; when it is
+    # not below `us`, the loop is bound by the host's launches, not the GPU
+    # the same calls from a HIP graph, and a plain read of the same byte count
+    # from a graph: the GPU's time per call without the host's launch work
+    g_us = graph_us(torch, lambda k, st: dm.expert_ffn(layer, k % E, x1, out=out1, ws=ws1,
+                                                       stream=st))
+    buf = torch.empty(16 * eb, dtype=torch.uint8, device="cuda")  # 16 windows, 790 MB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    r_us = graph_us(torch, lambda k, st: dm.read_probe(buf[(k % 16) * eb:], eb, sink, stream=st))
+    del buf
+    res["one_expert_bsz1"] = {"us": us, "hbm_gbps": eb / (us * 1e-6) / 1e9, "bytes": eb,
+                              "host_us_per_call": host_us,
+                              "graph_us": g_us, "graph_hbm_gbps": eb / (g_us * 1e-6) / 1e9,
+                              "read_probe_graph_us": r_us,
+                              "vs_read_probe": r_us / g_us}
     n = steps + warmup
     X = torch.from_numpy(np.stack([synth.activations(SEED, WORKLOAD, 0, 60_000 + s, 2, H)
                                    for s in range(n)])).cuda()
@@ -500,16 +580,13 @@ def time_expert_and_partials(torch, dm, layer, steps, warmup):
     by = float(np.mean([(len(np.unique(p)) + 1) * eb for p, _ in r[warmup:]]))
     outp = torch.empty((32, 2, H), dtype=torch.float32, device="cuda")
     wsp = layer.workspace(2, 32)
+    def part(s):
+        dm.moe_layer(layer, X[s], IDS[s], W[s], out=outp, n_shards=32, ws=wsp, stream=stream)
+
     for s in range(warmup):
-        dm.moe_layer(layer, X[s], IDS[s], W[s], out=outp, n_shards=32, ws=wsp, stream=stream)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for k in range(steps):
-        s = warmup + k
-        dm.moe_layer(layer, X[s], IDS[s], W[s], out=outp, n_shards=32, ws=wsp, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / steps
+        part(s)
+    us = back_to_back_us(torch, stream, steps, lambda k: part(warmup + k),
+                         lambda: part(max(warmup - 1, 0)))
     res["pair_32_partials_bsz2"] = {"us": us, "tokens_per_s": 2 / (us * 1e-6),
                                     "hbm_gbps": by / (us * 1e-6) / 1e9}
     log("expert / partials:", json.dumps(res))
@@ -533,18 +610,13 @@ def time_prefill(torch, dm, layer, T, steps, warmup, draws=4):
         uniq.append(len(np.unique(i)))
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = layer.prefill_workspace(T)
-    for s in range(warmup):
-        dm.moe_prefill(layer, xs[s % draws], ids[s % draws], ws_[s % draws], out=out, ws=ws,
-                       stream=stream)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for k in range(steps):
+    def call(k):
         d = k % draws
         dm.moe_prefill(layer, xs[d], ids[d], ws_[d], out=out, ws=ws, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    for s in range(warmup):
+        call(s)
+    ms = back_to_back_us(torch, stream, steps, call, lambda: call(draws - 1)) / 1e3
     eb = layer.expert_bytes()
     wbytes = float(np.mean([(u + 1) * eb for u in uniq]))
     flops = 2.0 * 3 * H * I * T * (K + 1)     # every (token, expert) pair: gate, up, down
@@ -573,16 +645,12 @@ def time_dense(torch, dm, steps, warmup):
                                        for s in range(8)])).cuda()
         out = torch.empty((T, H), dtype=torch.float32, device="cuda")
         ws = mlp.workspace(T)
+        def call(s):
+            dm.expert_ffn(mlp, 0, X[s % 8], out=out, ws=ws, stream=stream)
+
         for s in range(warmup):
-            dm.expert_ffn(mlp, 0, X[s % 8], out=out, ws=ws, stream=stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for s in range(steps):
-            dm.expert_ffn(mlp, 0, X[s % 8], out=out, ws=ws, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / steps
+            call(s)
+        us = back_to_back_us(torch, stream, steps, call, lambda: call(7))
         gbps = mlp.expert_bytes() / (us * 1e-6) / 1e9
         res["bsz%d" % T] = {"us": us, "tokens_per_s": T / (us * 1e-6), "hbm_gbps": gbps,
                             "hbm_frac": gbps / HBM_PEAK_GBPS}
@@ -622,17 +690,13 @@ def time_stack(torch, dm, steps, warmup):
         W = torch.from_numpy(np.stack(W).astype(np.float32)).cuda()
         out = torch.empty((T, H), dtype=torch.float32, device="cuda")
         ws = stack.workspace(T)
+        def call(s):
+            dm.moe_stack(stack, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
+
         for s in range(warmup):
-            dm.moe_stack(stack, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for k in range(steps):
-            s = warmup + k
-            dm.moe_stack(stack, X[s], IDS[s], W[s], out=out, ws=ws, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / steps
+            call(s)
+        ms = back_to_back_us(torch, stream, steps, lambda k: call(warmup + k),
+                             lambda: call(max(warmup - 1, 0))) / 1e3
         if not np.all(np.isfinite(out.cpu().numpy())):
             raise RuntimeError("non-finite stack output at bsz %d" % T)
         gb = float(np.mean(by[warmup:])) / 1e9

@@ -296,9 +296,9 @@ __device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const WavePlan &pl
 
 template <int P>
 __device__ __forceinline__ void gu_issue(GuTile<P> &b, const GuUnit &u, const LayerArgs &a,
-                                         int lane) {
+                                         int lane, bool live = true) {
   const uint32_t H = a.H, I = a.I;
-  const bool kv = u.kc + lane * 16 < H;
+  const bool kv = live && u.kc + lane * 16 < H;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -482,6 +482,109 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
     u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
   }
 #endif
+}
+
+// Single-expert calls whose I / P tasks would leave more than half of the
+// persistent grid idle (one expert of 2048 rows against 16 waves on each of
+// 256 CUs): each task is split along the hidden dimension between the two
+// waves of a pair in one workgroup.  Wave 2j of the grid takes the first
+// ceil(nc / 2) 1024-wide chunks of task j, wave 2j + 1 the rest; a wave keeps
+// up to three chunks' loads in flight.  The pair's row sums meet in LDS and
+// are added in a fixed order (first half + second half) before SwiGLU, so the
+// result does not depend on timing.  Needs 2 * (I / P) <= all waves.
+template <int TG, int P, int WA>
+__global__ __launch_bounds__(WA * 64) void k_gate_up_split(const LayerArgs a, const int t0) {
+  extern __shared__ float4 xs4[];  // [TG][nc * 256], as in k_gate_up
+  __shared__ float comb[WA / 2][2][P][TG];
+  constexpr int NT = WA * 64;
+  constexpr int XR = 8;
+  const int H = a.H, H4 = a.H / 4;
+  const int nc = (H + kChunk - 1) / kChunk;
+  const int Hp4 = nc * (kChunk / 4);
+  const int n4 = TG * Hp4;
+  const int NB = a.I / P;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * WA + wave;
+  const int task = gw >> 1, half = gw & 1;
+  const int cm = (nc + 1) / 2;
+  const int c_lo = half ? cm : 0;
+  const bool live = task < NB;
+  const int n = live ? (half ? nc - cm : cm) : 0;  // chunks of this wave
+
+  // x first, then the weights: the LDS staging waits for x only
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)t0 * H, (uint32_t)(TG * H) * 4u);
+  auto x_off = [&](int q) -> uint32_t {
+    const int t = q / Hp4, k4 = q - t * Hp4;
+    return (q < n4 && k4 < H4) ? (uint32_t)(t * H4 + k4) * 16u : kOutOfRange;
+  };
+  float4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) xr[j] = buf_loadf4(rx, x_off(threadIdx.x + j * NT));
+
+  const int e = a.single_expert;
+  GuUnit u = gu_unit<P>(a, e, live ? task : 0, c_lo);
+  auto unit = [&](int k) {  // chunk c_lo + k of the wave's task
+    GuUnit v = u;
+    v.c = c_lo + k;
+    v.kc = (uint32_t)(c_lo + k) * kChunk;
+    return v;
+  };
+  GuTile<P> b0, b1, b2;
+  gu_issue(b0, unit(0), a, lane, 0 < n);
+  gu_issue(b1, unit(1), a, lane, 1 < n);
+  gu_issue(b2, unit(2), a, lane, 2 < n);
+
+  if (blockIdx.x == 0 && wave == 0 && t0 == 0) plan_store(wave_plan(a, PlanIn{0, 0.0f}), a);
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int q = threadIdx.x + j * NT;
+    if (q < n4) xs4[q] = xr[j];
+  }
+  for (int q = threadIdx.x + XR * NT; q < n4; q += NT) xs4[q] = buf_loadf4(rx, x_off(q));
+  __syncthreads();
+
+  float acc[2][P][TG][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
+
+  for (int k = 0; k < n; k += 3) {
+    gu_consume<TG, P>(b0, xs4, Hp4, unit(k).kc, lane, acc);
+    gu_issue(b0, unit(k + 3), a, lane, k + 3 < n);
+    if (k + 1 >= n) break;
+    gu_consume<TG, P>(b1, xs4, Hp4, unit(k + 1).kc, lane, acc);
+    gu_issue(b1, unit(k + 4), a, lane, k + 4 < n);
+    if (k + 2 >= n) break;
+    gu_consume<TG, P>(b2, xs4, Hp4, unit(k + 2).kc, lane, acc);
+    gu_issue(b2, unit(k + 5), a, lane, k + 5 < n);
+  }
+
+  float gs[P][TG], vs[P][TG];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      gs[p][t] = wave_sum(acc[0][p][t][0] + acc[0][p][t][1]);
+      vs[p][t] = wave_sum(acc[1][p][t][0] + acc[1][p][t][1]);
+      if (half && lane == 0) {
+        comb[wave >> 1][0][p][t] = gs[p][t];
+        comb[wave >> 1][1][p][t] = vs[p][t];
+      }
+    }
+  __syncthreads();
+  if (half || !live || lane != 0) return;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float g = gs[p][t] + comb[wave >> 1][0][p][t];
+      const float v = vs[p][t] + comb[wave >> 1][1][p][t];
+      a.hbuf[(size_t)(t0 + t) * a.I + u.row0 + p] = silu(g) * v;
+    }
 }
 
 // ------------------------------------------------------------------ down ----
@@ -1443,7 +1546,21 @@ hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
   const int cus = cu_budget(a.cus);
   if (cus <= 0) return hipErrorInvalidConfiguration;
   per_cu = std::max(1, std::min(per_cu, DUCKMOE_GU_WAVES_PER_CU / WA));
-  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(WA * 64), lds, st, a, t0);
+  const int grid = cus * per_cu;
+  if (a.ids == nullptr && !a.in_rms && 2 * (a.I / P) <= grid * WA) {
+    // one expert: tasks split between wave pairs (same launch shape and LDS)
+    const auto split = k_gate_up_split<TG, P, WA>;
+    static OccCache occ_split;
+    int per_cu_split = 0;
+    err = occupancy(occ_split, split, WA * 64, lds, kGuXLds, per_cu_split);
+    if (err != hipSuccess) return err;
+    const int grid_split = cus * std::max(1, std::min(per_cu_split, DUCKMOE_GU_WAVES_PER_CU / WA));
+    if (2 * (a.I / P) <= grid_split * WA) {
+      hipLaunchKernelGGL(split, dim3(grid_split), dim3(WA * 64), lds, st, a, t0);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), lds, st, a, t0);
   return hipGetLastError();
 }
 

@@ -227,6 +227,33 @@ def test_small_layer_shard_partials(torch_dev, small_layers, n_shards):
     check_close(got.sum(axis=0), full, "sum of %d partials" % n_shards)
 
 
+@pytest.mark.parametrize("wl, T, n_shards", [
+    (100, 1, 1), (100, 2, 1), (101, 1, 1), (101, 2, 1), (102, 2, 4), (103, 5, 2), (103, 8, 16)])
+def test_small_expert_ffn(torch_dev, small_layers, wl, T, n_shards):
+    """One expert per call (its gate/up rows split between wave pairs when the
+    rows are fewer than half the waves): the routed expert 3 and the shared
+    expert against the oracle, hidden sizes of 2 and 3 chunks with ragged last
+    chunks, one to eight tokens, plain and as shard partials; a repeat call is
+    bit-identical."""
+    torch = torch_dev
+    lay, ox = small_layers[wl]
+    x = synth.activations(SEED, wl, 0, 700 + T, T, lay.hidden)
+    for e in (3, lay.n_routed):
+        say("small expert_ffn", wl, "expert", e, "T =", T, "n_shards =", n_shards)
+        ox.prefetch([e])
+        ws = lay.workspace(T, n_shards)
+        got = dm.expert_ffn(lay, e, to_dev(torch, x), n_shards=n_shards, ws=ws).cpu().numpy()
+        again = dm.expert_ffn(lay, e, to_dev(torch, x), n_shards=n_shards, ws=ws).cpu().numpy()
+        np.testing.assert_array_equal(got, again)
+        if n_shards == 1:
+            check_close(got, oracle.expert_ffn(ox(e), x), "expert %d T=%d" % (e, T))
+        else:
+            ref = oracle.moe_partials(lambda _: ox(e), x, np.zeros((T, 0), np.int64),
+                                      np.zeros((T, 0)), lay.n_routed, n_shards)
+            for r in range(n_shards):
+                check_close(got[r], ref[r], "expert %d shard %d/%d" % (e, r, n_shards))
+
+
 def first_appearance(ids, n_routed):
     """Distinct valid ids in order of first appearance (token-major)."""
     seen = []
