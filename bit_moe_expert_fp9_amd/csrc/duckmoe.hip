@@ -86,6 +86,7 @@ struct WsHeader {
   int32_t n_slots;
 };
 constexpr size_t kPlanOff = 256;   // int32 n_slots, then expert[slot]
+constexpr size_t kMaskOff = 640;   // int32 token mask of each slot (bit t: token t names it)
 
 struct LayerArgs {
   int H, I, n_routed, top_k, T, n_shards;
@@ -205,10 +206,26 @@ __device__ __forceinline__ float plan_weight(const WavePlan &p, const LayerArgs 
   return wt;
 }
 
+// Tokens t0 .. t0 + n - 1 that name slot s (bit t for token t0 + t): a token
+// that names no position of a routed slot has weight 0 there, so its h' for
+// the slot is 0 and its products can be skipped without changing any bit of
+// the output (fp9 weights are finite).  Slot 0 serves every token.  s uniform.
+__device__ __forceinline__ int slot_tokens(const WavePlan &p, const LayerArgs &a, int s, int t0,
+                                           int n) {
+  if (s == 0 || a.ids == nullptr) return (1 << n) - 1;
+  int m = 0;
+  for (int t = 0; t < n; ++t)
+    for (int i = 0; i < a.top_k; ++i)
+      if (__builtin_amdgcn_readlane(p.slot, (t0 + t) * a.top_k + i) == s) m |= 1 << t;
+  return m;
+}
+
 // The plan as the down launch reads it from the workspace: int32 n_slots, then
-// the expert of each slot.  Written by one wave.
+// the expert of each slot; at kMaskOff the token mask of each slot (all T
+// tokens).  Written by one wave.
 __device__ __forceinline__ void plan_store(const WavePlan &p, const LayerArgs &a) {
   int32_t *dst = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(a.hdr) + kPlanOff);
+  int32_t *msk = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(a.hdr) + kMaskOff);
   const int lane = threadIdx.x & 63;
   if (lane == 0) {
     a.hdr->status = p.status;
@@ -217,6 +234,17 @@ __device__ __forceinline__ void plan_store(const WavePlan &p, const LayerArgs &a
     dst[1] = p.e0;
   }
   if (lane < p.n_slots - 1) dst[2 + lane] = p.expert;
+  // lane s: the tokens naming slot s (a per-lane slot, so the loop compares
+  // every position's slot with the lane's own)
+  int m = 0;
+  if (lane == 0 || a.ids == nullptr) {
+    m = (1 << a.T) - 1;
+  } else {
+    const int N = a.T * a.top_k;
+    for (int j = 0; j < N; ++j)
+      if (__builtin_amdgcn_readlane(p.slot, j) == lane) m |= 1 << (j / a.top_k);
+  }
+  if (lane < p.n_slots) msk[lane] = m;
 }
 
 // The RMS glue's sum of squares of one row in a fixed order: thread j < 256
@@ -259,6 +287,7 @@ struct GuUnit {              // where one (task, chunk) unit reads from
   int slot;
   int task;
   int c;                     // chunk index
+  int tm;                    // tokens of the pass that name the slot (bit t), see slot_tokens
 };
 
 template <int P>
@@ -274,13 +303,15 @@ __device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, int e, int task, i
   u.slot = slot;
   u.task = task;
   u.c = c;
+  u.tm = -1;
   return u;
 }
 
-// The unit after u in a wave's sequence: next chunk, or chunk 0 of task + NW.
-template <int P>
+// The unit after u in a wave's sequence: next chunk, or chunk 0 of task + NW
+// (with, from two tokens on, the pass's tokens that name its slot).
+template <int TG, int P>
 __device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const WavePlan &plan,
-                                          const GuUnit &u, int nc, int NW, int ntask) {
+                                          const GuUnit &u, int nc, int NW, int ntask, int t0) {
   if (u.c + 1 < nc) {
     GuUnit n = u;
     n.c = u.c + 1;
@@ -288,7 +319,12 @@ __device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const WavePlan &pl
     return n;
   }
   const int t = u.task + NW;
-  if (t < ntask) return gu_unit<P>(a, plan_expert(plan, t / (a.I / P)), t, 0);
+  if (t < ntask) {
+    const int slot = t / (a.I / P);
+    GuUnit n = gu_unit<P>(a, plan_expert(plan, slot), t, 0);
+    if (TG > 1) n.tm = slot_tokens(plan, a, slot, t0, TG);
+    return n;
+  }
   GuUnit n = u;
   n.task = ntask;  // past the end
   return n;
@@ -309,12 +345,16 @@ __device__ __forceinline__ void gu_issue(GuTile<P> &b, const GuUnit &u, const La
     }
 }
 
+// tm: the tokens whose products are needed (bit t); the others' activations
+// are not read and their accumulators stay zero (uniform branches).
 template <int TG, int P>
 __device__ __forceinline__ void gu_consume(const GuTile<P> &b, const float4 *xs4, int Hp4,
-                                           uint32_t kc, int lane, float (&acc)[2][P][TG][2]) {
+                                           uint32_t kc, int lane, float (&acc)[2][P][TG][2],
+                                           int tm) {
   float xv[TG][16];
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
+    if (TG > 1 && !((tm >> t) & 1)) continue;
     const float4 *src = xs4 + t * Hp4 + kc / 4 + lane * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -332,7 +372,8 @@ __device__ __forceinline__ void gu_consume(const GuTile<P> &b, const float4 *xs4
       h2_t h[8];
       fp9_decode16(b.d[g][p], b.s[g][p], h);
 #pragma unroll
-      for (int t = 0; t < TG; ++t) fma16(h, xv[t], acc[g][p][t][0], acc[g][p][t][1]);
+      for (int t = 0; t < TG; ++t)
+        if (TG == 1 || ((tm >> t) & 1)) fma16(h, xv[t], acc[g][p][t][0], acc[g][p][t][1]);
     }
 }
 
@@ -402,6 +443,7 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
   if (!early) {
     if (gw < ntask) {
       u0 = gu_unit<P>(a, plan_expert(plan, gw / NB), gw, 0);
+      if (TG > 1) u0.tm = slot_tokens(plan, a, gw / NB, t0, TG);
       gu_issue(b0, u0, a, lane);
     } else {
       u0 = gu_unit<P>(a, plan.e0, 0, 0);
@@ -445,41 +487,41 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
 
   // The next DEPTH - 1 units' loads are in flight while a unit is computed.
   // DEPTH units per trip so that the register buffers keep static names.
-  GuUnit u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+  GuUnit u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
 #if DUCKMOE_GU_DEPTH == 3
   if (u1.task < ntask) gu_issue(b1, u1, a, lane);
   GuTile<P> b2;
   GuUnit u2;
   while (u0.task < ntask) {
-    u2 = gu_next<P>(a, plan, u1, nc, NW, ntask);
+    u2 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0);
     if (u2.task < ntask) gu_issue(b2, u2, a, lane);
-    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc);
+    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc, u0.tm);
     if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
     if (u1.task >= ntask) break;
 
-    u0 = gu_next<P>(a, plan, u2, nc, NW, ntask);
+    u0 = gu_next<TG, P>(a, plan, u2, nc, NW, ntask, t0);
     if (u0.task < ntask) gu_issue(b0, u0, a, lane);
-    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc);
+    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc, u1.tm);
     if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
     if (u2.task >= ntask) break;
 
-    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
     if (u1.task < ntask) gu_issue(b1, u1, a, lane);
-    gu_consume<TG, P>(b2, xs4, Hp4, u2.kc, lane, acc);
+    gu_consume<TG, P>(b2, xs4, Hp4, u2.kc, lane, acc, u2.tm);
     if (u2.c == nc - 1) gu_finish<TG, P>(a, plan, u2.slot, u2.row0, t0, lane, acc);
   }
 #else
   while (u0.task < ntask) {
     if (u1.task < ntask) gu_issue(b1, u1, a, lane);
-    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc);
+    gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc, u0.tm);
     if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
     if (u1.task >= ntask) break;
 
-    u0 = gu_next<P>(a, plan, u1, nc, NW, ntask);
+    u0 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0);
     if (u0.task < ntask) gu_issue(b0, u0, a, lane);
-    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc);
+    gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc, u1.tm);
     if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
-    u1 = gu_next<P>(a, plan, u0, nc, NW, ntask);
+    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
   }
 #endif
 }
@@ -553,13 +595,13 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_split(const LayerArgs a, co
       for (int t = 0; t < TG; ++t) acc[g][p][t][0] = acc[g][p][t][1] = 0.0f;
 
   for (int k = 0; k < n; k += 3) {
-    gu_consume<TG, P>(b0, xs4, Hp4, unit(k).kc, lane, acc);
+    gu_consume<TG, P>(b0, xs4, Hp4, unit(k).kc, lane, acc, -1);
     gu_issue(b0, unit(k + 3), a, lane, k + 3 < n);
     if (k + 1 >= n) break;
-    gu_consume<TG, P>(b1, xs4, Hp4, unit(k + 1).kc, lane, acc);
+    gu_consume<TG, P>(b1, xs4, Hp4, unit(k + 1).kc, lane, acc, -1);
     gu_issue(b1, unit(k + 4), a, lane, k + 4 < n);
     if (k + 2 >= n) break;
-    gu_consume<TG, P>(b2, xs4, Hp4, unit(k + 2).kc, lane, acc);
+    gu_consume<TG, P>(b2, xs4, Hp4, unit(k + 2).kc, lane, acc, -1);
     gu_issue(b2, unit(k + 5), a, lane, k + 5 < n);
   }
 
@@ -616,12 +658,13 @@ struct DnTile {
   uint4 d[R];
   DnSign<T> s[R];
   float4 h[T][4];  // the item's activations h'[slot][t][k .. k+16)
+  int tm;          // tokens naming the item's slot (bit t); the others' h' is 0
 };
 
 template <int T, int R>
 __device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, int e,
                                          __amdgpu_buffer_rsrc_t rh, int slot, int row0,
-                                         uint32_t k, bool kv) {
+                                         uint32_t k, bool kv, int tm) {
   const uint32_t H = a.H, I = a.I;
   const uint32_t mat = H * I;
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dn_body + (size_t)e * mat, mat);
@@ -633,12 +676,16 @@ __device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, in
     b.d[r] = buf_load16(rb, ok ? row * I + k : kOutOfRange);
     b.s[r] = (DnSign<T>)buf_load2h(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
   }
+  // h' rows of tokens that do not name the slot are zero: not read (the
+  // out-of-range loads return zeros without touching memory)
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const uint32_t off = kv ? ((uint32_t)(slot * a.T + t) * I + k) * 4u : kOutOfRange;
+    const bool tv = kv && (T == 1 || ((tm >> t) & 1));
+    const uint32_t off = tv ? ((uint32_t)(slot * a.T + t) * I + k) * 4u : kOutOfRange;
 #pragma unroll
     for (int j = 0; j < 4; ++j) b.h[t][j] = buf_loadf4(rh, off + 16 * j);
   }
+  b.tm = tm;
 }
 
 template <int T, int R>
@@ -655,12 +702,15 @@ __device__ __forceinline__ void dn_consume(const DnTile<T, R> &b, float (&acc)[R
       hv[t][4 * j + 3] = v.w;
     }
   }
+  // a token that does not name the slot would add 0 * w = 0 (fp9 weights are
+  // finite), so skipping it leaves every accumulator bit unchanged
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     h2_t h[8];
     fp9_decode16(b.d[r], b.s[r], h);
 #pragma unroll
-    for (int t = 0; t < T; ++t) fma16(h, hv[t], acc[r][t][0], acc[r][t][1]);
+    for (int t = 0; t < T; ++t)
+      if (T == 1 || ((b.tm >> t) & 1)) fma16(h, hv[t], acc[r][t][0], acc[r][t][1]);
   }
 }
 
@@ -683,7 +733,11 @@ __device__ __forceinline__ void dn_item(DnTile<T, R> &b, const LayerArgs &a, con
                                         int lane) {
   const int slot = q / nc;
   const uint32_t k = (uint32_t)(q - slot * nc) * kChunk + lane * 16;
-  dn_issue<T, R>(b, a, plan_at(plan, slot), rh, slot, row0, k, k < (uint32_t)a.I);
+  int tm = -1;
+  if (T > 1)  // the slot's token mask, stored with the plan
+    tm = __builtin_amdgcn_readfirstlane(
+        plan[(int)((kMaskOff - kPlanOff) / sizeof(int32_t)) + slot]);
+  dn_issue<T, R>(b, a, plan_at(plan, slot), rh, slot, row0, k, k < (uint32_t)a.I, tm);
 }
 
 template <int T, int R, int WB>
@@ -723,7 +777,7 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
   const bool first_now = wave < nc && (int)blockIdx.x < nblk;
   if (first_now) {
     const uint32_t k = (uint32_t)wave * kChunk + lane * 16;
-    dn_issue<T, R>(b0, a, slot0_expert(a), rh, 0, blockIdx.x * R, k, k < (uint32_t)I);
+    dn_issue<T, R>(b0, a, slot0_expert(a), rh, 0, blockIdx.x * R, k, k < (uint32_t)I, -1);
   }
   const int nq = __builtin_amdgcn_readfirstlane(plan[0]) * nc;  // items per block
   if (!first_now && wave < nq && (int)blockIdx.x < nblk)
