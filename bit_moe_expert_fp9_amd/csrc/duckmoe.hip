@@ -307,18 +307,37 @@ __device__ __forceinline__ GuUnit gu_unit(const LayerArgs &a, int e, int task, i
   return u;
 }
 
-// The unit after u in a wave's sequence: next chunk, or chunk 0 of task + NW
-// (with, from two tokens on, the pass's tokens that name its slot).
+// The unit after u in a wave's sequence: next chunk, or chunk 0 of the wave's
+// next task (with, from two tokens on, the pass's tokens that name its slot).
+//
+// Task order.  Tasks are dealt round robin: wave gw takes gw, gw + NW, ...  The
+// two workgroups a CU holds do not progress at the same rate: the one
+// dispatched first (blocks below gridDim.x / 2, waves below NW / 2) is served
+// first.  Per-wave timestamps at two tokens (17 slots, 8.5 tasks per wave)
+// had those waves, with 9 tasks each, end at a median of 82 us and the others,
+// with 8, at 95 us, the launch ending at ~100 us.  So in a two-token pass
+// (two workgroups per CU), when there are at least 4 rounds, the waves of the
+// later workgroups stop one round early and the earlier ones take that
+// round's tasks and the remainder with stride NW / 2 (10 against 7 tasks):
+// gate/up at two tokens 100.8 -> 99.3 us; moving two rounds measured worse
+// (103.0 us).  At one token the 5 / 4 split of the plain round robin already
+// ends both groups within 1 us.
+// Which wave computes a task does not change its result.
 template <int TG, int P>
 __device__ __forceinline__ GuUnit gu_next(const LayerArgs &a, const WavePlan &plan,
-                                          const GuUnit &u, int nc, int NW, int ntask, int t0) {
+                                          const GuUnit &u, int nc, int NW, int ntask, int t0,
+                                          int gw) {
   if (u.c + 1 < nc) {
     GuUnit n = u;
     n.c = u.c + 1;
     n.kc = u.kc + kChunk;
     return n;
   }
-  const int t = u.task + NW;
+  int t = u.task + NW;
+  if (TG == 2 && ntask / NW >= 4) {  // two tokens: two workgroups per CU
+    const int shared = (ntask / NW - 1) * NW;  // the rounds every wave takes
+    if (t >= shared) t = gw >= NW / 2 ? ntask : (u.task < shared ? shared + gw : u.task + NW / 2);
+  }
   if (t < ntask) {
     const int slot = t / (a.I / P);
     GuUnit n = gu_unit<P>(a, plan_expert(plan, slot), t, 0);
@@ -487,25 +506,25 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
 
   // The next DEPTH - 1 units' loads are in flight while a unit is computed.
   // DEPTH units per trip so that the register buffers keep static names.
-  GuUnit u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
+  GuUnit u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0, gw);
 #if DUCKMOE_GU_DEPTH == 3
   if (u1.task < ntask) gu_issue(b1, u1, a, lane);
   GuTile<P> b2;
   GuUnit u2;
   while (u0.task < ntask) {
-    u2 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0);
+    u2 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0, gw);
     if (u2.task < ntask) gu_issue(b2, u2, a, lane);
     gu_consume<TG, P>(b0, xs4, Hp4, u0.kc, lane, acc, u0.tm);
     if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
     if (u1.task >= ntask) break;
 
-    u0 = gu_next<TG, P>(a, plan, u2, nc, NW, ntask, t0);
+    u0 = gu_next<TG, P>(a, plan, u2, nc, NW, ntask, t0, gw);
     if (u0.task < ntask) gu_issue(b0, u0, a, lane);
     gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc, u1.tm);
     if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
     if (u2.task >= ntask) break;
 
-    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
+    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0, gw);
     if (u1.task < ntask) gu_issue(b1, u1, a, lane);
     gu_consume<TG, P>(b2, xs4, Hp4, u2.kc, lane, acc, u2.tm);
     if (u2.c == nc - 1) gu_finish<TG, P>(a, plan, u2.slot, u2.row0, t0, lane, acc);
@@ -517,11 +536,11 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up(const LayerArgs a, const in
     if (u0.c == nc - 1) gu_finish<TG, P>(a, plan, u0.slot, u0.row0, t0, lane, acc);
     if (u1.task >= ntask) break;
 
-    u0 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0);
+    u0 = gu_next<TG, P>(a, plan, u1, nc, NW, ntask, t0, gw);
     if (u0.task < ntask) gu_issue(b0, u0, a, lane);
     gu_consume<TG, P>(b1, xs4, Hp4, u1.kc, lane, acc, u1.tm);
     if (u1.c == nc - 1) gu_finish<TG, P>(a, plan, u1.slot, u1.row0, t0, lane, acc);
-    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0);
+    u1 = gu_next<TG, P>(a, plan, u0, nc, NW, ntask, t0, gw);
   }
 #endif
 }
