@@ -35,8 +35,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "c80c4905110d5448c72123e9521f3615925f45b9a974d3a538640ff1e8af0ed8",
-    "bytes_per_launch": 297744234,
+    "sources_sha256": "716c86e288034162a20f0d0cee8b74d1e96ad2cedabf2760bb9ac8fbee075e41",
+    "bytes_per_launch": 297744432,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
                   "bit_moe_expert_fp9_amd/csrc/mfma_device.h", "bit_moe_expert_fp9_amd/csrc/host_util.h")
