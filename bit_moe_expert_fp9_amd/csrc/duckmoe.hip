@@ -359,8 +359,8 @@ __device__ __forceinline__ void gu_issue(GuTile<P> &b, const GuUnit &u, const La
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t r = g * I + u.row0 + p;
-      b.d[g][p] = buf_load16(u.rb, kv ? r * H + u.kc + lane * 16 : kOutOfRange);
-      b.s[g][p] = buf_load2(u.rs, kv ? r * (H / 8) + (u.kc + lane * 16) / 8 : kOutOfRange);
+      b.d[g][p] = buf_load16<kStream>(u.rb, kv ? r * H + u.kc + lane * 16 : kOutOfRange);
+      b.s[g][p] = buf_load2<kStream>(u.rs, kv ? r * (H / 8) + (u.kc + lane * 16) / 8 : kOutOfRange);
     }
 }
 
@@ -692,8 +692,8 @@ __device__ __forceinline__ void dn_issue(DnTile<T, R> &b, const LayerArgs &a, in
   for (int r = 0; r < R; ++r) {
     const uint32_t row = row0 + r;
     const bool ok = kv && row < H;
-    b.d[r] = buf_load16(rb, ok ? row * I + k : kOutOfRange);
-    b.s[r] = (DnSign<T>)buf_load2h(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
+    b.d[r] = buf_load16<kStream>(rb, ok ? row * I + k : kOutOfRange);
+    b.s[r] = (DnSign<T>)buf_load2h<kStream>(rs, ok ? row * (I / 8) + k / 8 : kOutOfRange);
   }
   // h' rows of tokens that do not name the slot are zero: not read (the
   // out-of-range loads return zeros without touching memory)
@@ -1459,23 +1459,28 @@ __global__ __launch_bounds__(256) void k_rms(const float *x, int H, float eps, f
 }
 
 // Calibration: a plain streaming read of n1k blocks of 1 KB.  Wave w of the
-// grid reads a contiguous slab of blocks with 8 loads in flight and folds the
-// words into a value that is stored only if it matches a constant it never
-// matches, so the loads cannot be dropped.  This is the ceiling a pure weight
-// stream reaches on the device, the reference the layer kernels are held to.
+// grid reads a contiguous slab of blocks with 8 loads in flight (non-temporal,
+// the policy of the weight streams) and folds the words into a value that is
+// stored only if it matches a constant it never matches, so the loads cannot
+// be dropped.  This is the ceiling a pure weight stream reaches on the device,
+// the reference the layer kernels are held to.
 __global__ __launch_bounds__(512) void k_read_probe(const uint4 *__restrict__ p, uint32_t n1k,
                                                    uint32_t *sink) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
   const uint32_t nw = gridDim.x * (blockDim.x / 64);
   const uint32_t w = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t per = (n1k + nw - 1) / nw;
   const uint32_t b0 = min(n1k, w * per), b1 = min(n1k, b0 + per);
+  const u4v *q = reinterpret_cast<const u4v *>(p);
   uint32_t acc = 0;
   for (uint32_t b = b0; b < b1; b += 8) {
-    uint4 v[8];
+    u4v v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = (b + u < b1) ? p[(size_t)(b + u) * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < 8; ++u) {
+      v[u] = u4v{0u, 0u, 0u, 0u};
+      if (b + u < b1) v[u] = __builtin_nontemporal_load(q + (size_t)(b + u) * 64 + lane);
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }

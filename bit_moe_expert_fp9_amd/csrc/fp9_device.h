@@ -99,29 +99,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            (int)kBufCfg);
 }
 
+// Cache policy of a buffer load (the instruction's aux bits).  kStream sets
+// the non-temporal bit: plain streaming reads of a fresh 446 MB window with it
+// run at 6.8 TB/s on an MI355X against 6.06 TB/s without it (one launch, 32
+// waves per CU, 8 dwordx4 loads in flight per lane), and the bsz 1-2 decode
+// kernels, whose every weight load instruction covers whole 128-byte lines,
+// take it for their weight planes.  The matrix-core kernels read a line's
+// halves (and a row's sign bytes) with separate instructions; there the bit
+// made them 15-20% slower, so they keep the default policy, as do the
+// activations and plans, which are read again.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
 // The 128-bit results are reinterpreted as a whole vector: extracting and
 // bit-casting single elements (bit_cast<float>(v[i])) miscompiles with this
 // toolchain (one dword gets loaded and the offset register is read as data).
+template <int CP = kCached>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP));
 }
 
+template <int CP = kCached>
 __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
 }
 
 // The 16-bit result kept as 16 bits: widening it where it is used (not right
 // after the load) keeps the compiler from waiting for the load early.
+template <int CP = kCached>
 __device__ __forceinline__ uint16_t buf_load2h(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
 }
 
+template <int CP = kCached>
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP);
 }
 
+template <int CP = kCached>
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP));
 }
 
 __device__ __forceinline__ float4 buf_loadf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {

@@ -408,7 +408,7 @@ int duckmoe_moe_plan(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_rou
 /*
  * Calibration: a plain streaming read of `bytes` device bytes (16-byte
  * aligned buf, bytes a multiple of 1024; DUCKMOE_EINVAL otherwise) with
- * dwordx4 loads, 8 in flight per lane, 32 waves per CU.  It computes nothing
+ * non-temporal dwordx4 loads, 8 in flight per lane, 32 waves per CU.  It computes nothing
  * of the method; its duration is the read ceiling that the weight-streaming
  * kernels above are compared with.  sink: device uint32, written only in a case
  * that does not occur (it keeps the loads alive).
