@@ -1112,8 +1112,8 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
     for (int t = 0; t < RT; ++t) {
       const int row = r0 + 16 * t + (lane >> 2);
       const bool rv = live && row < I;
-      mx_load_body(bf.g[t], rb, (uint32_t)row, H, ch, rv);
-      mx_load_body(bf.u[t], rb, (uint32_t)(I + row), H, ch, rv);
+      mx_load_body_ln<kStream>(bf.g[t], rb, 0u, r0 + 16 * t, I, H, ch, live);
+      mx_load_body_ln<kStream>(bf.u[t], rb, (uint32_t)I, r0 + 16 * t, I, H, ch, live);
       if (half == 0) {
         mx_load_signs<SM>(sg.g[t], rs, (uint32_t)row, H, c0, rv);
         mx_load_signs<SM>(sg.u[t], rs, (uint32_t)(I + row), H, c0, rv);
@@ -1138,15 +1138,15 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   auto consume0 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
-      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
   };
   auto consume1 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg, MxItem it) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
-      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < np)) return;
     // close the task: partials to LDS, wave 0 reduces and writes h' (lane j < 8
@@ -1288,7 +1288,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = blk * 16 * RT + 16 * t + (lane >> 2);
-      mx_load_body(bf.w[t], rb, (uint32_t)row, I, ch, live && row < H);
+      mx_load_body_ln<kStream>(bf.w[t], rb, 0u, blk * 16 * RT + 16 * t, H, I, ch, live);
       if (half == 0) mx_load_signs<SM>(sg.w[t], rs, (uint32_t)row, I, c0, pl && row < H);
     }
     mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, ch, T, live);
@@ -1306,7 +1306,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.w[t], sg.w[t]), bf.b, d);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.w[t], sg.w[t]), bf.b, d);
       acc[t] += d * (sg.hs * part_scale);
     }
   };
@@ -1314,7 +1314,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.w[t], sg.w[t]), bf.b, d);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.w[t], sg.w[t]), bf.b, d);
       acc[t] += d * (sg.hs * part_scale);
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_pairs(it.task))) return;

@@ -65,23 +65,82 @@ struct MxFrag {     // the same unit moved to MFMA lane order
 // reads as zero, so they only choose the sign of a zero).  SA: the sign rows
 // are whole dwords (K % 32 == 0), so the four bytes are one dword load;
 // otherwise they are two 2-byte loads (dword loads must be dword-aligned; see
-// mx_sign_mode for the choice).
+// mx_sign_mode for the choice).  mx_load_sign_word is the sign part alone.
+template <bool SA>
+__device__ __forceinline__ uint32_t mx_load_sign_word(__amdgpu_buffer_rsrc_t rs, uint32_t row,
+                                                      uint32_t K, uint32_t c0, bool rv) {
+  const uint32_t q = threadIdx.x & 3;
+  const bool vs = rv && c0 + 32 * q < K;
+  const uint32_t so = row * (K / 8) + c0 / 8 + 4 * q;
+  if (SA) return buf_load4(rs, vs ? so : kOutOfRange);
+  const bool vs1 = rv && c0 + 32 * q + 16 < K;
+  return (uint32_t)buf_load2h(rs, vs ? so : kOutOfRange) |
+         ((uint32_t)buf_load2h(rs, vs1 ? so + 2 : kOutOfRange) << 16);
+}
+
 template <bool SA>
 __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
                                           __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
                                           uint32_t c0, bool rv) {
   const uint32_t q = threadIdx.x & 3;
   const uint32_t c = c0 + 16 * q;
-  const bool v0 = rv && c < K, v1 = rv && c + 64 < K, vs = rv && c0 + 32 * q < K;
+  const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
   w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
   w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
-  const uint32_t so = row * (K / 8) + c0 / 8 + 4 * q;
-  if (SA) {
-    w.s = buf_load4(rs, vs ? so : kOutOfRange);
+  w.s = mx_load_sign_word<SA>(rs, row, K, c0, rv);
+}
+
+// Whole-line body loads: lane 8r + q takes row r0 + r into b0 and row
+// r0 + 8 + r into b1, 16 bytes each at column c0 + 16q, so each load
+// instruction reads 8 rows x 128 contiguous bytes of the unit: whole 128-byte
+// lines.  The non-temporal policy needs that; with a line's halves in two
+// instructions (mx_load_w, mx_load_body) it reads slower than without it.
+// moff is added to every row index (the up half of a gate/up matrix); rows
+// r0 + r at or past `rows`, and all rows when live is false, read as zero.
+// W is MxTile or MxBody (only b0 and b1 are written).
+template <int CP, class W>
+__device__ __forceinline__ void mx_load_body_ln(W &w, __amdgpu_buffer_rsrc_t rb, uint32_t moff,
+                                                int r0, int rows, uint32_t K, uint32_t c0,
+                                                bool live) {
+  const int l = threadIdx.x & 63;
+  const int ra = r0 + (l >> 3), rc = ra + 8;
+  const uint32_t c = c0 + 16 * (l & 7);
+  const bool cv = live && c < K;
+  w.b0 = buf_load16<CP>(rb, cv && ra < rows ? (moff + (uint32_t)ra) * K + c : kOutOfRange);
+  w.b1 = buf_load16<CP>(rb, cv && rc < rows ? (moff + (uint32_t)rc) * K + c : kOutOfRange);
+}
+
+// Body words to MFMA lane order.  !LN (mx_load_w, mx_load_body): lane i + 16g
+// takes lane 4i + g's b0 and b1.  LN (mx_load_body_ln): lane i + 16g needs
+// row i's 16-byte chunks g (b0) and 4 + g (b1), held by lanes 8 (i % 8) + g and
+// 8 (i % 8) + 4 + g in their b0 (i < 8) or b1 (i >= 8).  Two moves per dword
+// carry them: in the first each lane sends b0 if its chunk is below 4, else
+// b1, and lane i + 16g reads lane 8 (i % 8) + g + 4 (i / 8); in the second the
+// other word, read from lane 8 (i % 8) + g + 4 (1 - i / 8).  Rows 0-7 receive
+// chunk g first, rows 8-15 chunk 4 + g.
+template <bool LN>
+__device__ __forceinline__ void mx_move_body(const uint4 &b0, const uint4 &b1, MxFrag &o) {
+  const int l = threadIdx.x & 63;
+  const int i = l & 15, g = l >> 4;
+  if (LN) {
+    const bool up = (l & 4) != 0, hi = i >= 8;
+    const int sA = 4 * (8 * (i & 7) + g + (hi ? 4 : 0));
+    const int sB = 4 * (8 * (i & 7) + g + (hi ? 0 : 4));
+    auto two = [&](uint32_t v0, uint32_t v1, uint32_t &d0, uint32_t &d1) {
+      const uint32_t a = (uint32_t)__builtin_amdgcn_ds_bpermute(sA, (int)(up ? v1 : v0));
+      const uint32_t b = (uint32_t)__builtin_amdgcn_ds_bpermute(sB, (int)(up ? v0 : v1));
+      d0 = hi ? b : a;
+      d1 = hi ? a : b;
+    };
+    two(b0.x, b1.x, o.b0.x, o.b1.x);
+    two(b0.y, b1.y, o.b0.y, o.b1.y);
+    two(b0.z, b1.z, o.b0.z, o.b1.z);
+    two(b0.w, b1.w, o.b0.w, o.b1.w);
   } else {
-    const bool vs1 = rv && c0 + 32 * q + 16 < K;
-    w.s = (uint32_t)buf_load2h(rs, vs ? so : kOutOfRange) |
-          ((uint32_t)buf_load2h(rs, vs1 ? so + 2 : kOutOfRange) << 16);
+    const int src = 4 * (4 * i + g);
+    auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
+    o.b0 = make_uint4(mv(b0.x), mv(b0.y), mv(b0.z), mv(b0.w));
+    o.b1 = make_uint4(mv(b1.x), mv(b1.y), mv(b1.z), mv(b1.w));
   }
 }
 
@@ -89,16 +148,14 @@ __device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
 // (see the layout note).  The empty volatile asm consumes the loaded sign word
 // here: without it the compiler may move work on it above an earlier barrier,
 // which makes that barrier wait for loads meant to stay in flight across it.
+template <bool LN = false>
 __device__ __forceinline__ MxFrag mx_to_mfma(const MxTile &w) {
   const int l = threadIdx.x & 63;
   const int i = l & 15, g = l >> 4;
-  const int src = 4 * (4 * i + g);  // byte address of lane 4i + g
-  auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
   uint32_t s = w.s;
   asm volatile("" : "+v"(s));
   MxFrag o;
-  o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
-  o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
+  mx_move_body<LN>(w.b0, w.b1, o);
   // bytes 2g, 2g + 1 sit in dword g / 2 of the row, bytes 8 + 2g, 9 + 2g in
   // dword 2 + g / 2; half g % 2 of each
   const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + (g >> 1)), (int)s);
@@ -174,17 +231,14 @@ __device__ __forceinline__ void mx_load_signs(MxSigns &s, __amdgpu_buffer_rsrc_t
 // per word first gathers, in v1, dword 0 / 1 of each unit on its even / odd
 // lane and, in v2, dword 2 / 3, so that each needed dword is one ds_bpermute
 // away.  In the other modes the unit's word is laid out as in mx_load_w.
-template <int SM, int HALF>
+template <int SM, int HALF, bool LN = false>
 __device__ __forceinline__ MxFrag mx_to_mfma_pair(const MxBody &w, const MxSigns &sp) {
   const int l = threadIdx.x & 63;
   const int i = l & 15, g = l >> 4;
-  const int src = 4 * (4 * i + g);
-  auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
   uint32_t sa = sp.a, sb = sp.b;
   asm volatile("" : "+v"(sa), "+v"(sb));
   MxFrag o;
-  o.b0 = make_uint4(mv(w.b0.x), mv(w.b0.y), mv(w.b0.z), mv(w.b0.w));
-  o.b1 = make_uint4(mv(w.b1.x), mv(w.b1.y), mv(w.b1.z), mv(w.b1.w));
+  mx_move_body<LN>(w.b0, w.b1, o);
   uint32_t x, y;
   if (SM == 2) {
     const bool odd = (l & 1) != 0;

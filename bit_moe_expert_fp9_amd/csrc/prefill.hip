@@ -83,6 +83,10 @@ constexpr int pf_q() { return TILE / 32; }      // token rows a thread stages pe
 #ifndef DUCKMOE_PF_DN_WG_PER_CU
 #define DUCKMOE_PF_DN_WG_PER_CU 1
 #endif
+#ifndef DUCKMOE_PF_WCP
+#define DUCKMOE_PF_WCP 2
+#endif
+constexpr int kPfWeightPolicy = DUCKMOE_PF_WCP;  // cache policy of the weight loads
 constexpr int kPfPitch = 2 * kMxUnit + 16;      // LDS bytes per token row of a unit (padded)
 constexpr int kPfMaxTopK = 32;
 constexpr int kPfMaxRouted = 1024;
@@ -498,10 +502,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     for (int r = 0; r < RT; ++r) {
       const int row = t.blk * kPfRows + wave * RT * 16 + 16 * r + (lane >> 2);
       const bool rv = row < rows && t.n > 0;
+      const int r0 = t.blk * kPfRows + wave * RT * 16 + 16 * r;
 #pragma unroll
-      for (int m = 0; m < M; ++m)
-        mx_load_w<SM == 1>(w[r][m], rb, rs, (uint32_t)(m * I + row), (uint32_t)Kd,
-                           (uint32_t)(u * kMxUnit), rv);
+      for (int m = 0; m < M; ++m) {
+        mx_load_body_ln<kPfWeightPolicy>(w[r][m], rb, (uint32_t)(m * I), r0, rows, (uint32_t)Kd,
+                                         (uint32_t)(u * kMxUnit), t.n > 0);
+        w[r][m].s = mx_load_sign_word<SM == 1>(rs, (uint32_t)(m * I + row), (uint32_t)Kd,
+                                               (uint32_t)(u * kMxUnit), rv);
+      }
     }
   };
   // form 2: the body of unit u, and (signs) the sign words of units u, u + 1
@@ -509,11 +517,11 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.body, mbytes);
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int row = t.blk * kPfRows + wave * RT * 16 + 16 * r + (lane >> 2);
-      const bool rv = row < rows && t.n > 0;
+      const int r0 = t.blk * kPfRows + wave * RT * 16 + 16 * r;
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        mx_load_body(w[r][m], rb, (uint32_t)(m * I + row), (uint32_t)Kd, (uint32_t)(u * kMxUnit), rv);
+        mx_load_body_ln<kPfWeightPolicy>(w[r][m], rb, (uint32_t)(m * I), r0, rows, (uint32_t)Kd,
+                                         (uint32_t)(u * kMxUnit), t.n > 0);
     }
   };
   auto load_signs = [&](MxSigns (&w)[RT][M], const PfTask<Q> &t, int u) {
@@ -577,14 +585,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma_pair<2, HALF>(rawb[r][m], sgn[r][m]);
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma_pair<2, HALF, true>(rawb[r][m], sgn[r][m]);
       load_body(rawb, nt, un);
       if (HALF == 1) load_signs(sgn, nt, un);  // un starts the next pair
     } else {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma<true>(raw[r][m]);
       load_w(raw, nt, un);
     }
     if (GU) {
