@@ -12,13 +12,14 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line(
-        "markers", "exhaustive: long exhaustive sweep, runs only with DUCKMOE_EXHAUSTIVE=1")
+        "markers", "exhaustive: exhaustive sweep (about a minute on 8 cores); "
+        "DUCKMOE_QUICK=1 skips it")
 
 
 def pytest_collection_modifyitems(config, items):
-    if os.environ.get("DUCKMOE_EXHAUSTIVE") == "1":
+    if os.environ.get("DUCKMOE_QUICK") != "1":
         return
-    skip = pytest.mark.skip(reason="exhaustive sweep: set DUCKMOE_EXHAUSTIVE=1 to run")
+    skip = pytest.mark.skip(reason="exhaustive sweep skipped (DUCKMOE_QUICK=1)")
     for item in items:
         if "exhaustive" in item.keywords:
             item.add_marker(skip)
