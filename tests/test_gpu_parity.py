@@ -414,6 +414,25 @@ def test_full_layer_bsz2_and_partials(torch_dev, v3_layer):
     check_close(parts.sum(axis=0), ref, "sum of 32 partials")
 
 
+def test_full_layer_matrix_core_batch_sizes(torch_dev, v3_layer):
+    """The matrix-core path (3 to 8 tokens) on the full 257-expert layer: one
+    draw of 7 tokens, its first T tokens for T = 3 .. 7 (bsz 8 has its own
+    test), each against the oracle on the same tokens."""
+    torch = torch_dev
+    lay, ox = v3_layer
+    x = synth.activations(SEED, 3, 0, 300, 7, H3)
+    ids, w = synth.routing(SEED, 3, 0, 300, 7, E3, K3)
+    ox.prefetch(list(ids.ravel()) + [E3])
+    for T in (3, 4, 5, 6, 7):
+        say("full layer, first", T, "tokens of a 7-token draw")
+        xt, it, wt = x[:T], ids[:T], w[:T]
+        ws = lay.workspace(T)
+        got = dm.moe_layer(lay, to_dev(torch, xt), to_dev(torch, it.astype(np.int32)),
+                           to_dev(torch, wt.astype(np.float32)), ws=ws).cpu().numpy()
+        assert dm.status(ws) == 0
+        check_close(got, oracle.moe_layer(ox, xt, it, wt, E3), "layer bsz%d" % T)
+
+
 def test_full_layer_bsz8_max_ids(torch_dev, v3_layer):
     torch = torch_dev
     lay, ox = v3_layer
