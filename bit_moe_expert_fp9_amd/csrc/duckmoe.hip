@@ -1138,15 +1138,15 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
   auto consume0 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
-      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
   };
   auto consume1 = [&](const GuMxBuf<RT> &bf, const GuMxSigns<RT> &sg, MxItem it) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
-      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.g[t], sg.g[t]), bf.b, acc[t][0]);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < np)) return;
     // close the task: partials to LDS, wave 0 reduces and writes h' (lane j < 8
@@ -1306,7 +1306,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 0, true>(bf.w[t], sg.w[t]), bf.b, d);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.w[t], sg.w[t]), bf.b, d);
       acc[t] += d * (sg.hs * part_scale);
     }
   };
@@ -1314,7 +1314,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 1, true>(bf.w[t], sg.w[t]), bf.b, d);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.w[t], sg.w[t]), bf.b, d);
       acc[t] += d * (sg.hs * part_scale);
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_pairs(it.task))) return;

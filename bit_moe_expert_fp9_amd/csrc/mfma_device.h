@@ -7,14 +7,14 @@
 // k % 8; the accumulator element D[i][j] in lane j + 16 * (i / 4), element i % 4.
 // The k index only has to agree between A and B.
 //
-// A unit is 128 columns of one 16-row tile.  It is loaded so that 4
-// consecutive lanes read 64 contiguous bytes of one row (lane 4i + q: row i,
-// columns 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15), which the memory
-// pipeline merges; ds_bpermute then moves lane 4i + g's words to lane i + 16g,
-// the MFMA's place for row i and lane group g.  After the move lane group g
-// holds columns 16g .. 16g + 15 (MFMA steps 0 and 1: 8 columns each) and
-// 64 + 16g .. 64 + 16g + 15 (steps 2 and 3), so in step s the group's 8
-// columns are 16g + 8 (s & 1) + 64 (s >> 1) .. + 7, and B must follow them.
+// A unit is 128 columns of one 16-row tile.  Its body is loaded in whole
+// 128-byte lines (mx_load_body_ln: lane 8r + q reads 16-byte chunk q of rows
+// r and r + 8), the form the non-temporal cache policy needs, and
+// ds_bpermute then gives lane i + 16g its row i's chunks g and 4 + g, the
+// MFMA's place for row i and lane group g.  Lane group g then holds columns
+// 16g .. 16g + 15 (MFMA steps 0 and 1: 8 columns each) and 64 + 16g ..
+// 64 + 16g + 15 (steps 2 and 3), so in step s the group's 8 columns are
+// 16g + 8 (s & 1) + 64 (s >> 1) .. + 7, and B must follow them.
 //
 // The unit's 16 sign bytes of row i are loaded as one dword per lane (lane
 // 4i + q: bytes 4q .. 4q + 3), 16 bytes per row in one request, instead of two
@@ -57,15 +57,14 @@ struct MxFrag {     // the same unit moved to MFMA lane order
   uint16_t s0, s1;  // their sign bits (16 + 16)
 };
 
-// Load lane 4i + q's share: row `row` (= the tile's row i), columns
-// c0 + 16q .. and c0 + 64 + 16q .. (16 each) of a [rows][K] matrix, and sign
-// bytes c0 / 8 + 4q .. + 3 of the row (columns c0 + 32q .. c0 + 32q + 31).
-// Rows with rv false and columns at or past K read as zero (a sign word that
-// starts below K may end past it; its extra bits belong to columns whose body
-// reads as zero, so they only choose the sign of a zero).  SA: the sign rows
-// are whole dwords (K % 32 == 0), so the four bytes are one dword load;
-// otherwise they are two 2-byte loads (dword loads must be dword-aligned; see
-// mx_sign_mode for the choice).  mx_load_sign_word is the sign part alone.
+// Lane 4i + q's sign word of a unit: bytes c0 / 8 + 4q .. + 3 of row `row`
+// (= the tile's row i) of a [rows][K] matrix, the signs of columns
+// c0 + 32q .. c0 + 32q + 31.  Rows with rv false and columns at or past K
+// read as zero (a sign word that starts below K may end past it; its extra
+// bits belong to columns whose body reads as zero, so they only choose the
+// sign of a zero).  SA: the sign rows are whole dwords (K % 32 == 0), so the
+// four bytes are one dword load; otherwise they are two 2-byte loads (dword
+// loads must be dword-aligned; see mx_sign_mode for the choice).
 template <bool SA>
 __device__ __forceinline__ uint32_t mx_load_sign_word(__amdgpu_buffer_rsrc_t rs, uint32_t row,
                                                       uint32_t K, uint32_t c0, bool rv) {
@@ -78,23 +77,11 @@ __device__ __forceinline__ uint32_t mx_load_sign_word(__amdgpu_buffer_rsrc_t rs,
          ((uint32_t)buf_load2h(rs, vs1 ? so + 2 : kOutOfRange) << 16);
 }
 
-template <bool SA>
-__device__ __forceinline__ void mx_load_w(MxTile &w, __amdgpu_buffer_rsrc_t rb,
-                                          __amdgpu_buffer_rsrc_t rs, uint32_t row, uint32_t K,
-                                          uint32_t c0, bool rv) {
-  const uint32_t q = threadIdx.x & 3;
-  const uint32_t c = c0 + 16 * q;
-  const bool v0 = rv && c < K, v1 = rv && c + 64 < K;
-  w.b0 = buf_load16(rb, v0 ? row * K + c : kOutOfRange);
-  w.b1 = buf_load16(rb, v1 ? row * K + c + 64 : kOutOfRange);
-  w.s = mx_load_sign_word<SA>(rs, row, K, c0, rv);
-}
-
 // Whole-line body loads: lane 8r + q takes row r0 + r into b0 and row
 // r0 + 8 + r into b1, 16 bytes each at column c0 + 16q, so each load
 // instruction reads 8 rows x 128 contiguous bytes of the unit: whole 128-byte
-// lines.  The non-temporal policy needs that; with a line's halves in two
-// instructions (mx_load_w, mx_load_body) it reads slower than without it.
+// lines.  The non-temporal policy needs that: with a line's two halves read by
+// two instructions it reads slower than without it.
 // moff is added to every row index (the up half of a gate/up matrix); rows
 // r0 + r at or past `rows`, and all rows when live is false, read as zero.
 // W is MxTile or MxBody (only b0 and b1 are written).
@@ -110,52 +97,42 @@ __device__ __forceinline__ void mx_load_body_ln(W &w, __amdgpu_buffer_rsrc_t rb,
   w.b1 = buf_load16<CP>(rb, cv && rc < rows ? (moff + (uint32_t)rc) * K + c : kOutOfRange);
 }
 
-// Body words to MFMA lane order.  !LN (mx_load_w, mx_load_body): lane i + 16g
-// takes lane 4i + g's b0 and b1.  LN (mx_load_body_ln): lane i + 16g needs
-// row i's 16-byte chunks g (b0) and 4 + g (b1), held by lanes 8 (i % 8) + g and
+// Body words (mx_load_body_ln) to MFMA lane order.  Lane i + 16g needs row i's
+// 16-byte chunks g (b0) and 4 + g (b1), held by lanes 8 (i % 8) + g and
 // 8 (i % 8) + 4 + g in their b0 (i < 8) or b1 (i >= 8).  Two moves per dword
 // carry them: in the first each lane sends b0 if its chunk is below 4, else
 // b1, and lane i + 16g reads lane 8 (i % 8) + g + 4 (i / 8); in the second the
 // other word, read from lane 8 (i % 8) + g + 4 (1 - i / 8).  Rows 0-7 receive
 // chunk g first, rows 8-15 chunk 4 + g.
-template <bool LN>
 __device__ __forceinline__ void mx_move_body(const uint4 &b0, const uint4 &b1, MxFrag &o) {
   const int l = threadIdx.x & 63;
   const int i = l & 15, g = l >> 4;
-  if (LN) {
-    const bool up = (l & 4) != 0, hi = i >= 8;
-    const int sA = 4 * (8 * (i & 7) + g + (hi ? 4 : 0));
-    const int sB = 4 * (8 * (i & 7) + g + (hi ? 0 : 4));
-    auto two = [&](uint32_t v0, uint32_t v1, uint32_t &d0, uint32_t &d1) {
-      const uint32_t a = (uint32_t)__builtin_amdgcn_ds_bpermute(sA, (int)(up ? v1 : v0));
-      const uint32_t b = (uint32_t)__builtin_amdgcn_ds_bpermute(sB, (int)(up ? v0 : v1));
-      d0 = hi ? b : a;
-      d1 = hi ? a : b;
-    };
-    two(b0.x, b1.x, o.b0.x, o.b1.x);
-    two(b0.y, b1.y, o.b0.y, o.b1.y);
-    two(b0.z, b1.z, o.b0.z, o.b1.z);
-    two(b0.w, b1.w, o.b0.w, o.b1.w);
-  } else {
-    const int src = 4 * (4 * i + g);
-    auto mv = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
-    o.b0 = make_uint4(mv(b0.x), mv(b0.y), mv(b0.z), mv(b0.w));
-    o.b1 = make_uint4(mv(b1.x), mv(b1.y), mv(b1.z), mv(b1.w));
-  }
+  const bool up = (l & 4) != 0, hi = i >= 8;
+  const int sA = 4 * (8 * (i & 7) + g + (hi ? 4 : 0));
+  const int sB = 4 * (8 * (i & 7) + g + (hi ? 0 : 4));
+  auto two = [&](uint32_t v0, uint32_t v1, uint32_t &d0, uint32_t &d1) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_ds_bpermute(sA, (int)(up ? v1 : v0));
+    const uint32_t b = (uint32_t)__builtin_amdgcn_ds_bpermute(sB, (int)(up ? v0 : v1));
+    d0 = hi ? b : a;
+    d1 = hi ? a : b;
+  };
+  two(b0.x, b1.x, o.b0.x, o.b1.x);
+  two(b0.y, b1.y, o.b0.y, o.b1.y);
+  two(b0.z, b1.z, o.b0.z, o.b1.z);
+  two(b0.w, b1.w, o.b0.w, o.b1.w);
 }
 
-// Move lane 4i + g's body words to lane i + 16g and gather its sign words
+// Move the body words to MFMA lane order and gather lane i + 16g's sign words
 // (see the layout note).  The empty volatile asm consumes the loaded sign word
 // here: without it the compiler may move work on it above an earlier barrier,
 // which makes that barrier wait for loads meant to stay in flight across it.
-template <bool LN = false>
 __device__ __forceinline__ MxFrag mx_to_mfma(const MxTile &w) {
   const int l = threadIdx.x & 63;
   const int i = l & 15, g = l >> 4;
   uint32_t s = w.s;
   asm volatile("" : "+v"(s));
   MxFrag o;
-  mx_move_body<LN>(w.b0, w.b1, o);
+  mx_move_body(w.b0, w.b1, o);
   // bytes 2g, 2g + 1 sit in dword g / 2 of the row, bytes 8 + 2g, 9 + 2g in
   // dword 2 + g / 2; half g % 2 of each
   const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + (g >> 1)), (int)s);
@@ -175,7 +152,7 @@ __device__ __forceinline__ MxFrag mx_to_mfma(const MxTile &w) {
 //   2: K % 64 == 0: one 8-byte load per lane, lane 4i + q taking bytes
 //      8q .. 8q + 7 of the pair's 32 (units 2p: q = 0, 1; 2p + 1: q = 2, 3);
 //      8-byte aligned, and a lane's 64 columns lie all below K or all past it;
-//   1: K % 32 == 0: one dword per lane and unit, as in mx_load_w;
+//   1: K % 32 == 0: one dword per lane and unit (mx_load_sign_word);
 //   0: two 2-byte loads per lane and unit.
 // The mode also needs the sign plane's base aligned to the load width (the
 // expert and row offsets then are: K % 16 == 0 for every matrix).
@@ -191,14 +168,6 @@ struct MxBody {     // one unit of one 16-row tile for one lane, as loaded
 struct MxSigns {    // the lane's sign words of a unit pair (layout by sign mode)
   uint32_t a, b;
 };
-
-// The body part of mx_load_w.
-__device__ __forceinline__ void mx_load_body(MxBody &w, __amdgpu_buffer_rsrc_t rb, uint32_t row,
-                                             uint32_t K, uint32_t c0, bool rv) {
-  const uint32_t c = c0 + 16 * (threadIdx.x & 3);
-  w.b0 = buf_load16(rb, rv && c < K ? row * K + c : kOutOfRange);
-  w.b1 = buf_load16(rb, rv && c + 64 < K ? row * K + c + 64 : kOutOfRange);
-}
 
 // The sign words of row `row` for the units starting at columns c0 and
 // c0 + 128; columns at or past K (and rows with rv false) read as zero.
@@ -230,15 +199,15 @@ __device__ __forceinline__ void mx_load_signs(MxSigns &s, __amdgpu_buffer_rsrc_t
 // (dwords 0, 1) and 4i + 2 HALF + 1 (dwords 2, 3); one quad-local DPP move
 // per word first gathers, in v1, dword 0 / 1 of each unit on its even / odd
 // lane and, in v2, dword 2 / 3, so that each needed dword is one ds_bpermute
-// away.  In the other modes the unit's word is laid out as in mx_load_w.
-template <int SM, int HALF, bool LN = false>
+// away.  In the other modes the unit's word is laid out as in mx_load_sign_word.
+template <int SM, int HALF>
 __device__ __forceinline__ MxFrag mx_to_mfma_pair(const MxBody &w, const MxSigns &sp) {
   const int l = threadIdx.x & 63;
   const int i = l & 15, g = l >> 4;
   uint32_t sa = sp.a, sb = sp.b;
   asm volatile("" : "+v"(sa), "+v"(sb));
   MxFrag o;
-  mx_move_body<LN>(w.b0, w.b1, o);
+  mx_move_body(w.b0, w.b1, o);
   uint32_t x, y;
   if (SM == 2) {
     const bool odd = (l & 1) != 0;

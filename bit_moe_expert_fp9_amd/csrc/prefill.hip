@@ -585,14 +585,14 @@ __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma_pair<2, HALF, true>(rawb[r][m], sgn[r][m]);
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma_pair<2, HALF>(rawb[r][m], sgn[r][m]);
       load_body(rawb, nt, un);
       if (HALF == 1) load_signs(sgn, nt, un);  // un starts the next pair
     } else {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma<true>(raw[r][m]);
+        for (int m = 0; m < M; ++m) wm[r][m] = mx_to_mfma(raw[r][m]);
       load_w(raw, nt, un);
     }
     if (GU) {
