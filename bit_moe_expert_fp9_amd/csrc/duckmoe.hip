@@ -20,7 +20,9 @@
 //   k_gate_up: persistent; each wave takes (expert slot, P intermediate rows)
 //     tasks in a strided sequence and walks the hidden dimension in
 //     1024-weight chunks: every lane loads 16 body bytes (one 128-bit load)
-//     and 2 sign bytes per row, decodes them in registers and FMAs them against
+//     and 2 sign bytes per row (non-temporal: a wave's load covers whole
+//     128-byte lines of a weight stream read once per call), decodes them in
+//     registers and FMAs them against
 //     the activation slice it reads from LDS (x is staged there once per
 //     workgroup).  At a task's end the wave sums its lanes with DPP, applies
 //     SwiGLU and the routing weight, and stores h' = w * silu(g) * v (f32) in
@@ -879,13 +881,13 @@ __global__ __launch_bounds__(WB * 64) void k_down(const LayerArgs a, const int G
 // Lane layout (checked on gfx950): A[i][k] is in lane i + 16 * (k / 8), element
 // k % 8; B[k][j] in lane j + 16 * (k / 8), element k % 8; the accumulator
 // element D[i][j] in lane j + 16 * (i / 4), element i % 4.  The k index only has
-// to agree between A and B.  Weights are loaded so that 4 consecutive lanes
-// read 64 contiguous bytes of one row (lane 4i + q: row i, columns
-// 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15 of the 128-column unit), which
-// the memory pipeline merges; ds_bpermute then moves lane 4i + g's words to
-// lane i + 16g, the MFMA's place for row i and lane group g.  So lane group g
-// holds columns 16g .. 16g + 15 (steps 0, 1) and 64 + 16g .. 64 + 16g + 15
-// (steps 2, 3), and the B loads follow the same columns.
+// to agree between A and B.  Weights are loaded in whole 128-byte lines, 8
+// lanes per row (lane 8r + q: 16-byte chunk q of rows r and r + 8 of the
+// 128-column unit), with the non-temporal policy; ds_bpermute then gives lane
+// i + 16g row i's chunks g and 4 + g, the MFMA's place for row i and lane
+// group g (mfma_device.h).  So lane group g holds columns 16g .. 16g + 15
+// (steps 0, 1) and 64 + 16g .. 64 + 16g + 15 (steps 2, 3), and the B loads
+// follow the same columns.
 constexpr int kMxGroups = 8;   // slot groups of the down pass (partials per row)
 constexpr float kLoScale = 2048.0f;
 
