@@ -625,7 +625,9 @@ def time_prefill(torch, dm, layer, T, steps, warmup, draws=4):
            "weight_hbm_frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
            "useful_tflops": flops / (ms * 1e-3) / 1e12,
            "useful_mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-           "mean_experts": float(np.mean(uniq)) + 1}
+           "mean_experts": float(np.mean(uniq)) + 1,
+           "dtype": "fp16 weights (exact fp9 decode) times scaled fp16 hi/lo activation pairs "
+                    "on the matrix cores, f32 accumulation"}
     log("prefill T=%d:" % T, json.dumps(res))
     return res
 
@@ -707,6 +709,9 @@ def time_stack(torch, dm, steps, warmup):
             "gb_per_pass": gb,
             "hbm_gbps": gb / (ms * 1e-3),
             "hbm_frac": gb / (ms * 1e-3) / HBM_PEAK_GBPS,
+            "dtype": ("f32: fp9 weights decoded to fp16, f32 multiply-add" if T <= 2 else
+                      "matrix-core path: fp16 weights (exact fp9 decode) times scaled fp16 "
+                      "hi/lo activation pairs, f32 accumulation"),
         }
         log("stack bsz%d:" % T, json.dumps(res[str(T)]))
         del X, IDS, W, ws
