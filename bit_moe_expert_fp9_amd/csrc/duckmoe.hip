@@ -991,6 +991,63 @@ __global__ __launch_bounds__(256) void k_mx_xprep(const LayerArgs a, const MxArg
   if (threadIdx.x == 0) m.xinv[t] = inv;
 }
 
+// A stack's glue between two layers on the matrix-core path, in one launch:
+// the previous layer's output row of token t (its kMxGroups down partials added
+// in group order, as k_mx_reduce adds them) is normalized by its RMS and split
+// as k_mx_xprep splits it.  The row is never written out; it sits in LDS so
+// that the sum of squares runs in rms_wave_part's order, and the results are
+// bit-identical to k_mx_reduce followed by k_mx_xprep.  One workgroup of 1024
+// threads per token; rows of up to kChainMaxH floats.
+constexpr int kChainMaxH = 8192;
+
+__global__ __launch_bounds__(1024) void k_mx_reduce_xprep(const LayerArgs a, const MxArgs m) {
+  __shared__ float4 row4[kChainMaxH / 4];
+  __shared__ float part[4];
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  const int n4 = a.H / 4, np4 = m.Hp / 4;
+  const size_t plane4 = (size_t)a.T * n4;  // float4s of one group's [T][H] partials
+  const float4 *p4 = reinterpret_cast<const float4 *>(m.part) + (size_t)t * n4;
+  float4 v[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + 1024 * q;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) {
+#pragma unroll
+      for (int g = 0; g < kMxGroups; ++g) {
+        const float4 p = p4[(size_t)g * plane4 + i];
+        s.x += p.x;
+        s.y += p.y;
+        s.z += p.z;
+        s.w += p.w;
+      }
+      row4[i] = s;
+    }
+    v[q] = s;
+  }
+  __syncthreads();
+  const float ss = rms_wave_part(reinterpret_cast<const float *>(row4), a.H);
+  if (threadIdx.x < 256 && (threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = rms_divisor(part, a.H, a.in_eps);
+  float mx = fmaxf(absmax4(v[0], r), absmax4(v[1], r));
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) mx = fmaxf(mx, red[w]);
+  const int k = mx_scale_exp(mx);
+  const float sc = ldexpf(1.0f, k);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + 1024 * q;
+    if (i < np4) mx_prep_store(v[q], r, sc, i, m.xb, a.T, t);
+  }
+  if (threadIdx.x == 0) m.xinv[t] = ldexpf(1.0f, -k);
+}
+
 // One workgroup per (slot, token) row of h' (rows of slots past the plan exit).
 __global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArgs m) {
   __shared__ float red[4];
@@ -1056,6 +1113,7 @@ struct MxItem {
   int task;
   int u;  // pair index, -1 for the empty pair
 };
+
 
 // Gate/up: a workgroup of WA waves takes whole tasks (slot, block of 16 * RT
 // rows) and splits the task's unit pairs (256 columns of H) over its waves; the
@@ -1705,8 +1763,13 @@ hipError_t launch_mx_gate_up_sm(const LayerArgs &a, const MxArgs &m, hipStream_t
   return hipSuccess;
 }
 
-hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
-  hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
+// chain_in: x is the previous layer's output, still as its down partials in
+// the same workspace (a stack's layers l > 0, H <= kChainMaxH, in_rms set).
+hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st, bool chain_in) {
+  if (chain_in)
+    hipLaunchKernelGGL(k_mx_reduce_xprep, dim3(a.T), dim3(1024), 0, st, a, m);
+  else
+    hipLaunchKernelGGL(k_mx_xprep, dim3(a.T), dim3(256), 0, st, a, m);
   const int sm = mx_sign_mode(a.H, a.gu_sign);
   const hipError_t err = sm == 2   ? launch_mx_gate_up_sm<2>(a, m, st)
                          : sm == 1 ? launch_mx_gate_up_sm<1>(a, m, st)
@@ -1730,23 +1793,35 @@ hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st
   return hipSuccess;
 }
 
-hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+// chain_out: the partials stay for the next layer's k_mx_reduce_xprep, and out
+// is not written.
+hipError_t launch_mx_down(const LayerArgs &a, const MxArgs &m, hipStream_t st, bool chain_out) {
   const int sm = mx_sign_mode(a.I, a.dn_sign);
   const hipError_t err = sm == 2   ? launch_mx_down_sm<2>(a, m, st)
                          : sm == 1 ? launch_mx_down_sm<1>(a, m, st)
                                    : launch_mx_down_sm<0>(a, m, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_mx_reduce, dim3((a.T * a.H + 255) / 256), dim3(256), 0, st, a, m);
+  if (!chain_out)
+    hipLaunchKernelGGL(k_mx_reduce, dim3((a.T * a.H + 255) / 256), dim3(256), 0, st, a, m);
   return hipGetLastError();
 }
 
 enum Stages { kGateUp = 1, kDown = 2, kBoth = 3 };
 
+// Stack chaining on the matrix-core path: kChainIn, the layer's input is the
+// previous layer's down partials in the same workspace; kChainOut, the layer
+// leaves its partials there instead of writing out.
+enum Chain { kChainIn = 1, kChainOut = 2 };
+
+bool chain_ok(const duckmoe_layer *L, int T) {
+  return use_mx(T, 1) && L->hidden <= kChainMaxH;
+}
+
 // Shared argument checks and dispatch of the layer entry points.
 int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const float *w,
               int single_expert, int32_t T, float *out, int32_t n_shards, void *ws,
               size_t ws_bytes, hipStream_t stream, int stages, int in_rms = 0,
-              float in_eps = 0.0f, int cus = 0) {
+              float in_eps = 0.0f, int cus = 0, int chain = 0) {
   int rc = check_layer(L);
   if (rc) return rc;
   const bool single = ids == nullptr;
@@ -1793,8 +1868,11 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
     m.part = reinterpret_cast<float *>(b + l.part);
     m.Hp = l.Hp;
     m.Ip = l.Ip;
-    if ((stages & kGateUp) && launch_mx_gate_up(a, m, stream) != hipSuccess) return DUCKMOE_EHIP;
-    if ((stages & kDown) && launch_mx_down(a, m, stream) != hipSuccess) return DUCKMOE_EHIP;
+    if ((stages & kGateUp) &&
+        launch_mx_gate_up(a, m, stream, (chain & kChainIn) && in_rms) != hipSuccess)
+      return DUCKMOE_EHIP;
+    if ((stages & kDown) && launch_mx_down(a, m, stream, chain & kChainOut) != hipSuccess)
+      return DUCKMOE_EHIP;
     return DUCKMOE_OK;
   }
   if (stages & kGateUp) {
@@ -1937,12 +2015,16 @@ int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float
                                              stack_act_bytes(L0, T))};
   // Layer l > 0 reads layer l-1's raw output and normalizes it in its gate/up
   // prologue (bit-identical to duckmoe_rms_normalize followed by the layer).
+  // On the matrix-core path the raw output is never written between layers:
+  // the next layer's first launch adds layer l-1's partials itself.
   const size_t per = (size_t)T * L0->top_k;
+  const bool chained = chain_ok(L0, T);
   const float *in = x;
   for (int l = 0; l < n_layers; ++l) {
     float *y = l == n_layers - 1 ? out : act[l & 1];
+    const int chain = !chained ? 0 : (l > 0 ? kChainIn : 0) | (l < n_layers - 1 ? kChainOut : 0);
     rc = run_layer(&layers[l], in, ids + l * per, w + l * per, 0, T, y, 1, ws,
-                   stack_act_off(L0, T), stream, kBoth, l > 0, eps);
+                   stack_act_off(L0, T), stream, kBoth, l > 0, eps, 0, chain);
     if (rc) return rc;
     in = y;
   }

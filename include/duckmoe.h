@@ -263,7 +263,10 @@ int duckmoe_rms_normalize(const float *x, int32_t T, int32_t H, float eps, float
  * The status word (duckmoe_status on ws) is that of the last layer.  The glue
  * runs inside the next layer's first kernel (no launch of its own) with the
  * same arithmetic in the same order, so the result equals calling
- * duckmoe_moe_layer and duckmoe_rms_normalize in turn, bit for bit.
+ * duckmoe_moe_layer and duckmoe_rms_normalize in turn, bit for bit.  At T >= 3
+ * with H <= 8192 that kernel also finishes the previous layer (its fixed-order
+ * sum of the down pass's partial results), so the inner layers' outputs y_l
+ * never go to memory: one launch fewer per layer.
  */
 size_t duckmoe_stack_workspace_bytes(const duckmoe_layer *layers, int32_t n_layers, int32_t T);
 int duckmoe_moe_stack(const duckmoe_layer *layers, int32_t n_layers, const float *x,

@@ -199,6 +199,22 @@ def test_small_stack(torch_dev, T):
                 [(l, list(range(T))) for l in range(NL)], "small stack T=%d" % T)
 
 
+@pytest.mark.parametrize("T,H,eps", [
+    (4, 1040, 1e-5),   # matrix-core layers: the next layer's first launch adds the partials
+    (3, 8320, 0.0),    # rows past 8192 floats: the partials are added and split in two launches
+    (5, 8320, 1e-5),
+])
+def test_stack_glue_forms(torch_dev, T, H, eps):
+    torch = torch_dev
+    I, E, K, NL, wl = 208, 12, 4, 3, 141
+    say("stack glue forms T =", T, "H =", H, "eps =", eps)
+    layers = [dm.Layer(H, I, E, K).fill_synthetic(SEED, wl, l) for l in range(NL)]
+    oxs = [OracleExperts(SEED, wl, l, H, I) for l in range(NL)]
+    x, ids, w = stack_inputs(wl, NL, T, E, K, H, 20 + T)
+    check_stack(torch, dm.Stack(layers), oxs, x, ids, w, eps,
+                [(l, list(range(T))) for l in range(NL)], "stack T=%d H=%d" % (T, H))
+
+
 # Workload 5: 16 layers x (256 routed + 1 shared) experts of 7168/2048, drawn on
 # the device (~204 GB of fp9 planes resident), run at bsz 1, 2, 4 and 8.
 FULL = dict(H=7168, I=2048, E=256, K=8, NL=16, wl=5)
