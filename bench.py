@@ -35,7 +35,7 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "7d35f1f77fdabdd50c5c6ba81646484be01f92834e45c21019c108bd38a2533a",
+    "sources_sha256": "235ce86188100681dedbf81b8f72d2e247dba2e4c633fb89c8f646fdda7692d5",
     "bytes_per_launch": 297741638,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
