@@ -36,10 +36,10 @@
 //     added in LDS in a fixed order: every output element is written once, no
 //     atomics, bit-reproducible run to run.
 // From 3 tokens on (no shard partials) the two contractions run on the matrix
-// cores instead (k_mx_xprep, k_gate_up_mx, k_mx_hprep, k_down_mx, k_mx_reduce):
-// the fp9 weights decode exactly to fp16 A tiles, the activations are split
-// into scaled fp16 hi and lo parts that share one B operand, and the sums are
-// recombined and unscaled in f32.
+// cores instead (k_mx_xprep, k_gate_up_mx, k_down_mx, k_mx_reduce): the fp9
+// weights decode exactly to fp16 A tiles, the activations are split into
+// scaled fp16 hi and lo parts that share one B operand (x by k_mx_xprep, h' by
+// the gate/up epilogue), and the sums are recombined and unscaled in f32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -901,10 +901,18 @@ struct MxArgs {
   _Float16 *xb;       // [Hp/8][2][T][8] scaled activations, hi and lo (zero padded)
   float *xinv;        // [T] 2^-k of each token's scale
   _Float16 *hb;       // [slots][Ip/8][2][T][8] scaled h'
-  float *hinv;        // [slots][T]
+  int8_t *hexp;       // [slots][T][EB] scale exponent of each 32-row block of h'
   float *part;        // [kMxGroups][T][H] down partials
   int Hp, Ip;         // H, I rounded up to whole units
+  int EB;             // exponent bytes per (slot, token): 8 per unit pair
 };
+
+// h' is scaled per (slot, token, block of kHBlock rows of I), the rows one
+// gate/up task owns, so each task's epilogue splits its own rows.  A block
+// whose rows are all zero takes exponent kZeroExp, so that it never sets the
+// common scale of a unit (below).
+constexpr int kHBlock = 32;
+constexpr int kZeroExp = 126;
 
 __device__ __forceinline__ void mx_split(float v, _Float16 &hi, _Float16 &lo) {
   hi = (_Float16)v;
@@ -1048,29 +1056,18 @@ __global__ __launch_bounds__(1024) void k_mx_reduce_xprep(const LayerArgs a, con
   if (threadIdx.x == 0) m.xinv[t] = ldexpf(1.0f, -k);
 }
 
-// One workgroup per (slot, token) row of h' (rows of slots past the plan exit).
-__global__ __launch_bounds__(256) void k_mx_hprep(const LayerArgs a, const MxArgs m) {
-  __shared__ float red[4];
-  const int32_t *plan = reinterpret_cast<const int32_t *>(
-      reinterpret_cast<const uint8_t *>(a.hdr) + kPlanOff);
-  const int slot = blockIdx.x / a.T, t = blockIdx.x - slot * a.T;
-  if (slot >= __builtin_amdgcn_readfirstlane(plan[0])) return;
-  const size_t rowi = (size_t)slot * a.T + t;
-  const size_t blk = (size_t)slot * 2 * a.T * m.Ip;  // the slot's [Ip/8][2][T][8] block
-  const float inv = mx_prep_row(a.hbuf + rowi * a.I, a.I, m.Ip, 1.0f, m.hb + blk, a.T, t, red);
-  if (threadIdx.x == 0) m.hinv[rowi] = inv;
-}
-
 struct MxAct {      // the lane's 32 B values of one unit (hi or lo of one token)
   uint4 v[4];
 };
 
 // B for lane (column j, group g): part j / 8 of token j % 8, columns
 // c0 + 16g + 8s (s = 0, 1) and c0 + 64 + 16g + 8(s - 2) (s = 2, 3), from a
-// [cols/8][2][T][8] block at byte base; zeros for tokens at or past T, and
-// everywhere when live is false (the loads are issued either way).
+// [cols/8][2][T][8] block at byte base; zeros for tokens at or past T, for
+// columns at or past ncol (CLIP), and everywhere when live is false (the
+// loads are issued either way).
+template <bool CLIP>
 __device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t r, uint32_t base,
-                                          uint32_t c0, int T, bool live) {
+                                          uint32_t c0, int T, bool live, uint32_t ncol) {
   const int j = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
   const uint32_t row = (uint32_t)(j >> 3) * (uint32_t)T + (uint32_t)(j & 7);
   const bool v = live && (j & 7) < T;
@@ -1078,7 +1075,7 @@ __device__ __forceinline__ void mx_load_b(MxAct &b, __amdgpu_buffer_rsrc_t r, ui
   for (int s = 0; s < 4; ++s) {
     const uint32_t kb = (c0 + 16 * g) / 8 + (s & 1) + 8 * (s >> 1);
     const uint32_t o = base + (kb * 2u * (uint32_t)T + row) * 16u;
-    b.v[s] = buf_load16(r, v ? o : kOutOfRange);
+    b.v[s] = buf_load16(r, v && (!CLIP || kb * 8u < ncol) ? o : kOutOfRange);
   }
 }
 
@@ -1132,6 +1129,7 @@ struct GuMxSigns {
 
 template <int WA, int RT, int SM>
 __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const MxArgs m) {
+  static_assert(16 * RT == kHBlock, "a gate/up task owns one scale block of h' rows");
   __shared__ f4v_t red[2][WA][RT * 2][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1179,7 +1177,7 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
         mx_load_signs<SM>(sg.u[t], rs, (uint32_t)(I + row), H, c0, rv);
       }
     }
-    mx_load_b(bf.b, rx, 0u, ch, T, live);
+    mx_load_b<false>(bf.b, rx, 0u, ch, T, live, 0u);
   };
 
   f4v_t acc[RT][2];  // gate, up
@@ -1209,8 +1207,10 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
       mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.u[t], sg.u[t]), bf.b, acc[t][1]);
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < np)) return;
-    // close the task: partials to LDS, wave 0 reduces and writes h' (lane j < 8
-    // adds the hi sums of its own column and the lo sums of column 8 + j)
+    // close the task: partials to LDS, wave 0 reduces them and writes the
+    // block's h' as scaled hi/lo parts with the block's exponent per token (lane
+    // j < 8 adds the hi sums of its own column and the lo sums of column 8 + j;
+    // lanes j + 16g, g < 4, hold token j's 32 rows)
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1224,6 +1224,8 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
         const float w_t = plan_weight(plan, a, slot, t);
         if (t == j) wt = w_t;
       }
+      float hv[RT][4];
+      float mx = 0.0f;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         f4v_t G = {0, 0, 0, 0}, Gl = G, U = G, Ul = G;
@@ -1235,15 +1237,32 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
             U += red[parity][w][2 * t + 1][lane];
             Ul += red[parity][w][2 * t + 1][lane + 8];
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = r0 + 16 * t + 4 * g + r;
-            const float gs = (G[r] + Gl[r] * (1.0f / kLoScale)) * xs;
-            const float us = (U[r] + Ul[r] * (1.0f / kLoScale)) * xs;
-            const float hv = (wt == 0.0f) ? 0.0f : wt * (silu(gs) * us);
-            if (row < I) a.hbuf[((size_t)slot * T + j) * I + row] = hv;
-          }
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + 16 * t + 4 * g + r;
+          const float gs = (G[r] + Gl[r] * (1.0f / kLoScale)) * xs;
+          const float us = (U[r] + Ul[r] * (1.0f / kLoScale)) * xs;
+          hv[t][r] = (!jv || wt == 0.0f || row >= I) ? 0.0f : wt * (silu(gs) * us);
+          mx = fmaxf(mx, fabsf(hv[t][r]));
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const int k = mx > 0.0f ? mx_scale_exp(mx) : kZeroExp;
+      if (jv) {
+        const float sc = ldexpf(1.0f, k);
+        _Float16 *dst = m.hb + (size_t)slot * 2 * T * m.Ip;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          mx_prep_store(make_float4(hv[t][0], hv[t][1], hv[t][2], hv[t][3]), 1.0f, sc,
+                        (r0 + 16 * t + 4 * g) / 4, dst, T, j);
+        int8_t *ex = m.hexp + ((size_t)slot * T + j) * m.EB;
+        if (g == 0) ex[r0 / kHBlock] = (int8_t)k;
+        // blocks past the last one (to the end of the unit pair) hold no rows:
+        // the all-zero exponent keeps them out of their unit's common scale
+        if (r0 / kHBlock == NB - 1)
+          for (int q = NB + g; q < m.EB; q += 4) ex[q] = (int8_t)kZeroExp;
       }
     }
     parity ^= 1;
@@ -1274,8 +1293,9 @@ __global__ __launch_bounds__(WA * 64) void k_gate_up_mx(const LayerArgs a, const
 
 // Down: a workgroup takes tasks (block of 16 * RT rows of H, slot group q) and
 // splits the (slot, unit pair of I) items of the group's slots over its waves;
-// each unit's accumulator is unscaled into the wave's running sum (column j by
-// the token's scale, column 8 + j by that scale times 2^-11); the waves' sums
+// each unit's B values are first brought to the unit's common scale
+// (mx_unit_rescale), and its accumulator is unscaled into the wave's running
+// sum (column j by that scale, column 8 + j by it times 2^-11); the waves' sums
 // meet in LDS and wave 0 writes the group's partial for the block's rows,
 // adding columns j and 8 + j.  The groups' partials are added by k_mx_reduce in
 // a fixed order.
@@ -1288,11 +1308,45 @@ struct DnMxBuf {
 template <int RT>
 struct DnMxSigns {
   MxSigns w[RT];
-  float hs;  // the (slot, token) row's unscale factor, for both units
+  uint2 ex;  // exponents of the 8 h' blocks of the pair's two units, the lane's token
 };
 
+// 2^-d (d >= 0) as two fp16 halves: normal to d = 14, subnormal to 24, then 0.
+__device__ __forceinline__ uint32_t pow2neg_h2(int d) {
+  const uint32_t h = d <= 14 ? (uint32_t)(15 - d) << 10 : (d <= 24 ? 1u << (24 - d) : 0u);
+  return h | (h << 16);
+}
+
+__device__ __forceinline__ uint4 mul_h2(uint4 v, uint32_t f) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  const h2v m = __builtin_bit_cast(h2v, f);
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, v.x) * m),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, v.y) * m),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, v.z) * m),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, v.w) * m));
+}
+
+// One unit of h' as B: its 4 blocks were scaled by 2^e0 .. 2^e3 (signed bytes
+// of ew); lane group g's steps 0, 1 hold block g / 2 and steps 2, 3 block
+// 2 + g / 2.  Each value is brought to the unit's common scale 2^ku, ku the
+// smallest exponent (the block with the largest magnitude), by an exact
+// power-of-two step, and 2^-ku is returned to unscale the unit's products.
+__device__ __forceinline__ float mx_unit_rescale(MxAct &b, uint32_t ew, int g) {
+  const int e0 = (int8_t)(ew & 0xff), e1 = (int8_t)((ew >> 8) & 0xff);
+  const int e2 = (int8_t)((ew >> 16) & 0xff), e3 = (int8_t)(ew >> 24);
+  const int ku = min(min(e0, e1), min(e2, e3));
+  const uint32_t fa = pow2neg_h2(((g >> 1) ? e1 : e0) - ku);
+  const uint32_t fb = pow2neg_h2(((g >> 1) ? e3 : e2) - ku);
+  b.v[0] = mul_h2(b.v[0], fa);
+  b.v[1] = mul_h2(b.v[1], fa);
+  b.v[2] = mul_h2(b.v[2], fb);
+  b.v[3] = mul_h2(b.v[3], fb);
+  return ldexpf(1.0f, -max(-126, min(126, ku)));
+}
+
 template <int WA, int RT, int SM>
-__global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const MxArgs m) {
+__global__ __launch_bounds__(WA * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void k_down_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT][64];
   const int32_t *plan = reinterpret_cast<const int32_t *>(
       reinterpret_cast<const uint8_t *>(a.hdr) + kPlanOff);
@@ -1315,7 +1369,7 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   const uint32_t mat = (uint32_t)I * (uint32_t)H;
   const int max_slots = a.ids != nullptr ? T * a.top_k + 1 : 1;
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(m.hb, (uint32_t)(max_slots * 2 * T * m.Ip) * 2u);
-  const __amdgpu_buffer_rsrc_t rhs = make_rsrc(m.hinv, (uint32_t)(max_slots * T) * 4u);
+  const __amdgpu_buffer_rsrc_t rex = make_rsrc(m.hexp, (uint32_t)(max_slots * T * m.EB));
   // pairs of the task's group: (slot q + s * G, unit pair vp) for s < ns_q, vp < npv
   auto n_pairs = [&](int task) {
     const int q = task / NBH;
@@ -1351,10 +1405,10 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
       mx_load_body_ln<kStream>(bf.w[t], rb, 0u, blk * 16 * RT + 16 * t, H, I, ch, live);
       if (half == 0) mx_load_signs<SM>(sg.w[t], rs, (uint32_t)row, I, c0, pl && row < H);
     }
-    mx_load_b(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, ch, T, live);
+    mx_load_b<true>(bf.b, rh, (uint32_t)(slot * 2 * T * m.Ip) * 2u, ch, T, live, (uint32_t)I);
     if (half == 0)
-      sg.hs = __builtin_bit_cast(float, buf_load4(rhs, pl && bv ? (uint32_t)(slot * T + (j & 7)) * 4u
-                                                               : kOutOfRange));
+      sg.ex = buf_load8(rex, pl && bv ? (uint32_t)((slot * T + (j & 7)) * m.EB + 8 * vp)
+                                      : kOutOfRange);
   };
 
   f4v_t acc[RT];
@@ -1363,19 +1417,23 @@ __global__ __launch_bounds__(WA * 64) void k_down_mx(const LayerArgs a, const Mx
   int parity = 0;
 
   auto consume0 = [&](const DnMxBuf<RT> &bf, const DnMxSigns<RT> &sg) {  // empty items add zeros
+    MxAct b = bf.b;
+    const float hs = mx_unit_rescale(b, sg.ex.x, g) * part_scale;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.w[t], sg.w[t]), bf.b, d);
-      acc[t] += d * (sg.hs * part_scale);
+      mx_mma_frag(mx_to_mfma_pair<SM, 0>(bf.w[t], sg.w[t]), b, d);
+      acc[t] += d * hs;
     }
   };
   auto consume1 = [&](const DnMxBuf<RT> &bf, const DnMxSigns<RT> &sg, MxItem it) {
+    MxAct b = bf.b;
+    const float hs = mx_unit_rescale(b, sg.ex.y, g) * part_scale;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f4v_t d = {0, 0, 0, 0};
-      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.w[t], sg.w[t]), bf.b, d);
-      acc[t] += d * (sg.hs * part_scale);
+      mx_mma_frag(mx_to_mfma_pair<SM, 1>(bf.w[t], sg.w[t]), b, d);
+      acc[t] += d * hs;
     }
     if (it.task >= ntask || (it.u >= 0 && it.u + WA < n_pairs(it.task))) return;
 #pragma unroll
@@ -1638,8 +1696,8 @@ bool use_mx(int T, int n_shards) { return T >= DUCKMOE_MX_MIN_T && n_shards == 1
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct MxLayout {
-  size_t xb, xinv, hb, hinv, part, end;
-  int Hp, Ip;
+  size_t xb, xinv, hb, hexp, part, end;
+  int Hp, Ip, EB;
 };
 
 MxLayout mx_layout(const duckmoe_layer *L, int T, bool single, size_t base) {
@@ -1650,8 +1708,9 @@ MxLayout mx_layout(const duckmoe_layer *L, int T, bool single, size_t base) {
   size_t off = align256(base);
   m.xb = off;   off = align256(off + (size_t)2 * T * m.Hp * 2);
   m.xinv = off; off = align256(off + (size_t)T * 4);
+  m.EB = (m.Ip / kMxUnit + 1) / 2 * 8;
   m.hb = off;   off = align256(off + slots * 2 * T * m.Ip * 2);
-  m.hinv = off; off = align256(off + slots * T * 4);
+  m.hexp = off; off = align256(off + slots * T * m.EB);
   m.part = off; off = align256(off + (size_t)kMxGroups * T * L->hidden * 4);
   m.end = off;
   return m;
@@ -1775,8 +1834,6 @@ hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st
                          : sm == 1 ? launch_mx_gate_up_sm<1>(a, m, st)
                                    : launch_mx_gate_up_sm<0>(a, m, st);
   if (err != hipSuccess) return err;
-  const int max_slots = a.ids != nullptr ? a.T * a.top_k + 1 : 1;
-  hipLaunchKernelGGL(k_mx_hprep, dim3(max_slots * a.T), dim3(256), 0, st, a, m);
   return hipGetLastError();
 }
 
@@ -1864,10 +1921,11 @@ int run_layer(const duckmoe_layer *L, const float *x, const int32_t *ids, const 
     m.xb = reinterpret_cast<_Float16 *>(b + l.xb);
     m.xinv = reinterpret_cast<float *>(b + l.xinv);
     m.hb = reinterpret_cast<_Float16 *>(b + l.hb);
-    m.hinv = reinterpret_cast<float *>(b + l.hinv);
+    m.hexp = reinterpret_cast<int8_t *>(b + l.hexp);
     m.part = reinterpret_cast<float *>(b + l.part);
     m.Hp = l.Hp;
     m.Ip = l.Ip;
+    m.EB = l.EB;
     if ((stages & kGateUp) &&
         launch_mx_gate_up(a, m, stream, (chain & kChainIn) && in_rms) != hipSuccess)
       return DUCKMOE_EHIP;
