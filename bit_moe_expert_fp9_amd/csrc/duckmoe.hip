@@ -1344,8 +1344,8 @@ __device__ __forceinline__ float mx_unit_rescale(MxAct &b, uint32_t ew, int g) {
   return ldexpf(1.0f, -max(-126, min(126, ku)));
 }
 
-template <int WA, int RT, int SM>
-__global__ __launch_bounds__(WA * 64) __attribute__((amdgpu_waves_per_eu(4)))
+template <int WA, int RT, int SM, int WPE>
+__global__ __launch_bounds__(WA * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_down_mx(const LayerArgs a, const MxArgs m) {
   __shared__ f4v_t red[2][WA][RT][64];
   const int32_t *plan = reinterpret_cast<const int32_t *>(
@@ -1684,8 +1684,13 @@ size_t hbuf_bytes(const duckmoe_layer *L, int T, bool single) {
 #ifndef DUCKMOE_MX_GU_ROW_TILES
 #define DUCKMOE_MX_GU_ROW_TILES 2   // 16-row MFMA tiles per gate/up task (they share B loads)
 #endif
-#ifndef DUCKMOE_MX_DN_ROW_TILES
-#define DUCKMOE_MX_DN_ROW_TILES 2   // 16-row MFMA tiles per down task
+// Down task shapes: 16-row MFMA tiles per task (they share the B loads) and
+// the waves per SIMD the registers must allow.  Below DUCKMOE_MX_DN_WIDE_T
+// tokens 2 tiles at 4 waves; from it on 3 tiles at 3 waves (150 registers; 3
+// tiles at 4 waves spill), which measured 0.4-1% faster at 6-8 tokens and
+// the same at 5.
+#ifndef DUCKMOE_MX_DN_WIDE_T
+#define DUCKMOE_MX_DN_WIDE_T 6
 #endif
 #ifndef DUCKMOE_MX_WAVES_PER_CU
 #define DUCKMOE_MX_WAVES_PER_CU 16  // target resident waves per CU (capped by occupancy)
@@ -1837,10 +1842,10 @@ hipError_t launch_mx_gate_up(const LayerArgs &a, const MxArgs &m, hipStream_t st
   return hipGetLastError();
 }
 
-template <int SM>
-hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
-  constexpr int WA = DUCKMOE_MX_DN_WAVES, RT = DUCKMOE_MX_DN_ROW_TILES;
-  const auto kern = k_down_mx<WA, RT, SM>;
+template <int SM, int RT, int WPE>
+hipError_t launch_mx_down_shape(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  constexpr int WA = DUCKMOE_MX_DN_WAVES;
+  const auto kern = k_down_mx<WA, RT, SM, WPE>;
   static OccCache occ;
   int grid = 0;
   hipError_t err = persistent_grid(occ, kern, WA * 64, DUCKMOE_MX_WAVES_PER_CU,
@@ -1848,6 +1853,12 @@ hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WA * 64), 0, st, a, m);
   return hipSuccess;
+}
+
+template <int SM>
+hipError_t launch_mx_down_sm(const LayerArgs &a, const MxArgs &m, hipStream_t st) {
+  return a.T >= DUCKMOE_MX_DN_WIDE_T ? launch_mx_down_shape<SM, 3, 3>(a, m, st)
+                                      : launch_mx_down_shape<SM, 2, 4>(a, m, st);
 }
 
 // chain_out: the partials stay for the next layer's k_mx_reduce_xprep, and out
