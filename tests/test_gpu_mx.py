@@ -220,3 +220,42 @@ def test_sign_plane_alignment(torch_dev, offset):
     for t in (0, 35, 69):
         check_close(aligned[1][t], oracle.moe_layer(ox, xp[t:t + 1], idp[t:t + 1], wp[t:t + 1], E)[0],
                     "aligned prefill token %d" % t)
+
+
+# Blocks of 32 gate/up rows scaled apart: h' is scaled per (slot, token, block
+# of 32 rows) and the down pass brings the four blocks of each 128-row unit to
+# the unit's common scale.  Gate and up rows scaled by s give h' near s^2 times
+# the others, so within one unit blocks sit 2^-12 (exact step), 2^-18 (a
+# subnormal fp16 step) and 2^-24 or less (flushed, far below the bar) under the
+# largest; one block is all zero (its exponent must not set the unit's scale);
+# the ragged last unit is uniformly small (the unit's own scale is large), and
+# its blocks past I carry the all-zero exponent.  Token rows of x are scaled
+# 2^12 and 2^-12 apart.
+MIX_BLOCK_SCALE = {1: 2.0 ** -6, 2: 2.0 ** -9, 4: 0.0, 5: 2.0 ** -12, 7: 2.0 ** -3,
+                   8: 2.0 ** -6, 9: 2.0 ** -6, 10: 2.0 ** -6}
+
+
+@pytest.mark.parametrize("T", [3, 6, 8])
+def test_h_blocks_of_mixed_magnitude(torch_dev, T):
+    torch = torch_dev
+    wl, E2, K2 = 105, 6, 4
+    say("matrix-core path T =", T, "h' blocks of mixed magnitude")
+    lay = dm.Layer(H, I, E2, K2)
+    codes = {}
+    for e in range(E2 + 1):
+        g, u, d = (synth.weights(SEED, wl, 0, e, m, shp)
+                   for m, shp in enumerate(synth.expert_shapes(H, I)))
+        for b, s in MIX_BLOCK_SCALE.items():
+            g[32 * b:32 * (b + 1)] *= s
+            u[32 * b:32 * (b + 1)] *= s
+        lay.set_expert(e, g, u, d)
+        codes[e] = (oracle.quantize(g), oracle.quantize(u), oracle.quantize(d))
+    x = synth.activations(SEED, wl, 0, 30 + T, T, H)
+    x[0] *= 2.0 ** 12
+    x[1] *= 2.0 ** -12
+    ids, w = synth.routing(SEED, wl, 0, 30 + T, T, E2, K2)
+    got, st = call(torch, lay, x, ids, w)
+    assert st == 0
+    ref = oracle.moe_layer(lambda e: codes[int(e)], x, ids, w, E2)
+    for t in range(T):
+        check_close(got[t], ref[t], "mixed h' blocks T=%d token %d" % (T, t))
