@@ -1766,9 +1766,11 @@ hipError_t launch_gate_up_t(const LayerArgs &a, int t0, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int T>
-hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
-  constexpr int R = down_rows<T>();
+#ifndef DUCKMOE_DN_ROWS_SINGLE
+#define DUCKMOE_DN_ROWS_SINGLE 4
+#endif
+template <int T, int R>
+hipError_t launch_down_tr(const LayerArgs &a, hipStream_t st) {
   const auto kern = k_down<T, R, kWB>;
   const size_t lds = (size_t)kWB * R * T * 16 * sizeof(float);
   static OccCache occ;
@@ -1783,6 +1785,19 @@ hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWB * 64), lds, st, a,
                      group_width(a.I, a.n_shards));
   return hipGetLastError();
+}
+
+// One slot of at most two 1024-wide chunks (a single expert of the DeepSeek-V3
+// shape) gives a block of down_rows<1>() rows only two items, one per wave,
+// and the grid then holds half the resident waves: such calls take smaller
+// blocks.
+template <int T>
+hipError_t launch_down_t(const LayerArgs &a, hipStream_t st) {
+  if constexpr (T == 1) {
+    if (a.ids == nullptr && a.I <= 2 * kChunk)
+      return launch_down_tr<1, DUCKMOE_DN_ROWS_SINGLE>(a, st);
+  }
+  return launch_down_tr<T, down_rows<T>()>(a, st);
 }
 
 hipError_t launch_gate_up(const LayerArgs &a, hipStream_t st) {
