@@ -35,8 +35,8 @@ METRIC = "MoE-layer tokens/s at bsz=1/2 and achieved HBM GB/s (% of MI355X peak)
 # each scaled by the same counter's reading for a 1 GiB device copy (profiles/
 # moe_layer_hbm_counters.md).  Valid only for the kernel sources it was taken on.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "7c8a8d3ad8c038178dd8561e13442cf0a1ab630657a3b5d2a443b1051cda116e",
-    "bytes_per_launch": 297764260,
+    "sources_sha256": "580f596975f465ccc6f32c2615b7b280abd234600fd35204c1691dd88bada7d4",
+    "bytes_per_launch": 297756021,
 }
 KERNEL_SOURCES = ("bit_moe_expert_fp9_amd/csrc/duckmoe.hip", "bit_moe_expert_fp9_amd/csrc/fp9_device.h",
                   "bit_moe_expert_fp9_amd/csrc/mfma_device.h", "bit_moe_expert_fp9_amd/csrc/host_util.h")
