@@ -201,6 +201,7 @@ def test_small_stack(torch_dev, T):
 
 @pytest.mark.parametrize("T,H,eps", [
     (4, 1040, 1e-5),   # matrix-core layers: the next layer's first launch adds the partials
+    (6, 1040, 0.0),    # the same with three row tiles per down task
     (3, 8320, 0.0),    # rows past 8192 floats: the partials are added and split in two launches
     (5, 8320, 1e-5),
 ])
