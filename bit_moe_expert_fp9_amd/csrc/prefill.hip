@@ -131,30 +131,46 @@ __device__ __forceinline__ int block_sum256(int v, int *red) {
 }
 
 // ------------------------------------------------------------------ plan ----
+// The K ids of token t, loaded together (every load issued before any is
+// used; -1 past K).  KM >= K bounds the unrolled loops, so that the ids stay
+// in registers: 8, 16 or kPfMaxTopK (chosen by launch_plan).
+template <int KM>
+__device__ __forceinline__ void pf_row_ids(const PfArgs &a, int t, int (&v)[KM]) {
+  const int32_t *row = a.ids + (size_t)t * a.K;
+#pragma unroll
+  for (int i = 0; i < KM; ++i) v[i] = i < a.K ? row[i] : -1;
+}
+
 // One workgroup per list.  List 0 (shared) counts every token and checks every
 // token's ids (status word; -1 in tok_entry for repeats and bad ids); list
 // p >= 1 counts the tokens naming expert p - 1.  Counts go to off[p + 1].
+template <int KM>
 __global__ __launch_bounds__(256) void k_pf_count(const PfArgs a) {
   __shared__ int red[4];
   const int p = blockIdx.x, K = a.K, T = a.T;
   if (p == 0) {
     int st = 0;
     for (int t = threadIdx.x; t < T; t += 256) {
-      const int32_t *row = a.ids + (size_t)t * K;
-      for (int i = 0; i < K; ++i) {
-        const int id = row[i];
-        bool keep = id >= 0 && id < a.E;
-        if (!keep) {
-          st |= DUCKMOE_STATUS_BAD_ID;
-        } else {
-          for (int q = 0; q < i; ++q)
-            if (row[q] == id) {
+      int v[KM];
+      pf_row_ids(a, t, v);
+#pragma unroll
+      for (int i = 0; i < KM; ++i) {
+        if (i < K) {
+          const int id = v[i];
+          bool keep = id >= 0 && id < a.E;
+          if (!keep) {
+            st |= DUCKMOE_STATUS_BAD_ID;
+          } else {
+            bool dup = false;
+#pragma unroll
+            for (int q = 0; q < i; ++q) dup |= v[q] == id;
+            if (dup) {
               keep = false;
               st |= DUCKMOE_STATUS_DUP_ID;
-              break;
             }
+          }
+          if (!keep) a.tok_entry[(size_t)t * (K + 1) + 1 + i] = -1;
         }
-        if (!keep) a.tok_entry[(size_t)t * (K + 1) + 1 + i] = -1;
       }
     }
     const int bad = block_sum256((st & DUCKMOE_STATUS_BAD_ID) ? 1 : 0, red);
@@ -168,9 +184,11 @@ __global__ __launch_bounds__(256) void k_pf_count(const PfArgs a) {
   const int e = p - 1;
   int c = 0;
   for (int t = threadIdx.x; t < T; t += 256) {
-    const int32_t *row = a.ids + (size_t)t * K;
+    int v[KM];
+    pf_row_ids(a, t, v);
     bool hit = false;
-    for (int i = 0; i < K; ++i) hit |= row[i] == e;
+#pragma unroll
+    for (int i = 0; i < KM; ++i) hit |= v[i] == e;
     c += hit ? 1 : 0;
   }
   c = block_sum256(c, red);
@@ -220,6 +238,7 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const PfArgs a) {
 // One workgroup per list: the list's tokens in ascending order, 256 at a time;
 // a token's rank is the hits before it (ballot within the wave, wave counts
 // across the workgroup).
+template <int KM>
 __global__ __launch_bounds__(256) void k_pf_fill(const PfArgs a) {
   __shared__ int wc[4];
   const int p = blockIdx.x, K = a.K, T = a.T;
@@ -241,10 +260,12 @@ __global__ __launch_bounds__(256) void k_pf_fill(const PfArgs a) {
     int first = 0;
     float s = 0.0f;
     if (t < T) {
-      const int32_t *row = a.ids + (size_t)t * K;
+      int v[KM];
+      pf_row_ids(a, t, v);
       const float *wr = a.w + (size_t)t * K;
-      for (int i = 0; i < K; ++i) {
-        if (row[i] == e) {
+#pragma unroll
+      for (int i = 0; i < KM; ++i) {
+        if (v[i] == e) {
           if (!hit) first = i;
           hit = true;
           s += wr[i];
@@ -848,10 +869,22 @@ int pf_check(const duckmoe_layer *L, int T, bool routed) {
 }
 
 
-hipError_t launch_plan(const PfArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(k_pf_count, dim3(a.E + 1), dim3(256), 0, st, a);
+template <int KM>
+void launch_plan_km(const PfArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pf_count<KM>, dim3(a.E + 1), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(k_pf_fill, dim3(a.E + 1), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pf_fill<KM>, dim3(a.E + 1), dim3(256), 0, st, a);
+}
+
+// The plan kernels unroll their loops over a token's ids to the smallest
+// bound of 8, 16 and kPfMaxTopK that holds K.
+hipError_t launch_plan(const PfArgs &a, hipStream_t st) {
+  if (a.K <= 8)
+    launch_plan_km<8>(a, st);
+  else if (a.K <= 16)
+    launch_plan_km<16>(a, st);
+  else
+    launch_plan_km<kPfMaxTopK>(a, st);
   return hipGetLastError();
 }
 

@@ -60,25 +60,26 @@ def test_plan_bit_exact(torch_dev):
     torch = torch_dev
     rng = np.random.default_rng(41)
     for T, k, E in [(1, 8, 256), (7, 8, 256), (300, 8, 256), (2048, 8, 256), (517, 3, 9),
-                    (64, 1, 1), (1000, 32, 1024), (5, 8, 1024)]:
+                    (64, 1, 1), (1000, 32, 1024), (5, 8, 1024), (200, 12, 64), (33, 16, 16),
+                    (90, 17, 40)]:
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
         w = rng.random((T, k)).astype(np.float32)
         check_plan(torch, ids, w, E)
 
 
-def test_plan_repeats_and_bad_ids(torch_dev):
+@pytest.mark.parametrize("T,k,E,rep", [(333, 6, 11, (4, 1)), (150, 20, 40, (19, 17))])
+def test_plan_repeats_and_bad_ids(torch_dev, T, k, E, rep):
     torch = torch_dev
     rng = np.random.default_rng(42)
-    T, k, E = 333, 6, 11
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
     w = rng.random((T, k)).astype(np.float32)
     dup = ids.copy()
-    dup[::7, 4] = dup[::7, 1]                    # a repeat: weights add (one f32 add)
+    dup[::7, rep[0]] = dup[::7, rep[1]]          # a repeat: weights add (one f32 add)
     check_plan(torch, dup, w, E, status=dm.duckmoe.STATUS_DUP_ID)
     bad = ids.copy()
-    bad[5, 2], bad[100, 3] = -3, E + 4           # skipped: for the oracle a zero-weight
+    bad[5, 2], bad[100, k - 1] = -3, E + 4       # skipped: for the oracle a zero-weight
     ref_ids, ref_w = bad.copy(), w.copy()        # repeat of the token's first id
-    for t, i in ((5, 2), (100, 3)):
+    for t, i in ((5, 2), (100, k - 1)):
         ref_ids[t, i] = ids[t, 0]
         ref_w[t, i] = 0.0
     check_plan(torch, bad, w, E, ref_ids, ref_w, status=dm.duckmoe.STATUS_BAD_ID)
