@@ -327,7 +327,7 @@ def time_gate_up_back_to_back(torch, dm, layer, T, steps, warmup, draws):
 
 
 def time_gemv_256x512(torch, dm, reps=2000):
-    """Workload 1: one fp9 GEMV 256 x 512 (N(0, 0.02) weights, x ~ N(0, 1)) and
+    """One fp9 GEMV 256 x 512 (N(0, 0.02) weights, x ~ N(0, 1)) and
     the decode of all 512 fp9 codes, each as back-to-back launches between two
     events: launch-bound, reported in microseconds per call."""
     from bit_moe_expert_fp9_amd import synth

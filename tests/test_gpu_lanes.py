@@ -3,7 +3,7 @@
 A lane's layer must equal the plain duckmoe_moe_layer call bit for bit (same
 kernels, its own stream and workspace), must not start before the producer
 stream has written its input, and its output must be visible to a consumer
-stream after finish.  The full-size case runs the pair of workload 4 (two
+stream after finish.  The full-size case runs the bsz-2 pair (two
 tokens with independent top-8 sets on the 257-expert layer) as two lanes.
 """
 

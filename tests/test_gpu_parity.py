@@ -75,7 +75,7 @@ def test_decode_ragged_length(torch_dev):
 
 
 def test_gemv_single_fp9_matrix(torch_dev):
-    """Workload 1: W 256x512 ~ N(0, 0.02) in fp9, x ~ N(0, 1)."""
+    """One fp9 GEMV: W 256x512 ~ N(0, 0.02) in fp9, x ~ N(0, 1)."""
     torch = torch_dev
     say("gemv 256x512")
     W = synth.weights(SEED, 1, 0, 0, 0, (256, 512))
@@ -370,7 +370,7 @@ def v3_layer(torch_dev):
 
 
 def test_expert_ffn_full_size(torch_dev, v3_layer):
-    """Workload 2's expert shape: one SwiGLU expert 7168/2048 at bsz 1, plus
+    """One SwiGLU expert 7168/2048 at bsz 1 (a routed expert), plus
     the shared expert at bsz 2 and its 32 partials."""
     torch = torch_dev
     lay, ox = v3_layer
@@ -398,7 +398,7 @@ def test_full_layer_bsz1(torch_dev, v3_layer, step):
 
 
 def test_full_layer_bsz2_and_partials(torch_dev, v3_layer):
-    """Workload 4: two tokens with independent top-8 sets; then 32 partials of
+    """The bsz-2 pair: two tokens with independent top-8 sets; then 32 partials of
     64-wide intermediate slices whose sum is the full output."""
     torch = torch_dev
     lay, ox = v3_layer

@@ -5,8 +5,8 @@ and packer; f32 outputs within relative L2 <= 1e-5 and max-abs <= 1e-4 *
 max|ref| of the float64 oracle.  The stack is checked per layer with teacher
 forcing: the oracle gets the GPU's input to layer l and its output is compared
 with the GPU's output of layer l; the native stack call must equal the same
-layers and glue called one by one, bit for bit.  Workload 5 is the full-size
-stack: 16 layers of 7168/2048 with 256 routed + 1 shared experts each (about
+layers and glue called one by one, bit for bit.  The full-size
+stack is 16 layers of 7168/2048 with 256 routed + 1 shared experts each (about
 204 GB of fp9 weights resident), drawn on the device.
 """
 
@@ -216,7 +216,7 @@ def test_stack_glue_forms(torch_dev, T, H, eps):
                 [(l, list(range(T))) for l in range(NL)], "stack T=%d H=%d" % (T, H))
 
 
-# Workload 5: 16 layers x (256 routed + 1 shared) experts of 7168/2048, drawn on
+# The full-size stack: 16 layers x (256 routed + 1 shared) experts of 7168/2048, drawn on
 # the device (~204 GB of fp9 planes resident), run at bsz 1, 2, 4 and 8.
 FULL = dict(H=7168, I=2048, E=256, K=8, NL=16, wl=5)
 
